@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for GQA flash attention (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package. It shares no code with the HIP path.
+"""
+
+from .attention import (  # noqa: F401
+    attention_ref,
+    combine_ref,
+    decode_paged_ref,
+    paged_gather_ref,
+    partial_attention_ref,
+    to_f64,
+    visible_mask,
+)

@@ -1,0 +1,54 @@
+"""Plausible mistakes planted in copies of the oracle (on the CPU) must each
+be caught by the pin battery: this shows the pins constrain every part of
+the oracle that the GPU path is compared against."""
+
+import os
+import types
+
+import pytest
+
+from tests.oracle_pins import ALL_CHECKS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTATIONS = {
+    "gqa head map h % Hkv": ("g = h // group", "g = h % Hkv"),
+    "causal off by one": ("j[None, :] <= pos[:, None]", "j[None, :] < pos[:, None]"),
+    "window off by one": ("(pos[:, None] - j[None, :]) < window", "(pos[:, None] - j[None, :]) <= window"),
+    "top-left causal alignment": ("pos = rows + (skv - sq)", "pos = rows"),
+    "scale dropped": ("s = scale * (q_rows @ k.T)", "s = (q_rows @ k.T)"),
+    "lse without max": ("m_safe + np.log(np.where(empty, 1.0, l))", "np.log(np.where(empty, 1.0, l))"),
+    "no normalisation": ("num / np.where(empty, 1.0, l)[:, None]", "num"),
+    "combine lse without max": ("M_safe + np.log(np.where(empty, 1.0, tot))", "np.log(np.where(empty, 1.0, tot))"),
+    "combine unnormalised weights": ("w / np.where(empty, 1.0, tot)[..., None]", "w"),
+    "gather slot index": ("out[b, t] = cache[page, t % page_size]", "out[b, t] = cache[page, t // page_size % page_size]"),
+    "seq_lens ignored": ("skv = seq_lens[b]", "skv = Skv"),
+    "empty row lse": ("lse = np.where(empty, -np.inf,", "lse = np.where(empty, 0.0,"),
+}
+
+
+def _load_mutant(old, new):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmutated_oracle_passes_battery():
+    import oracle
+    for check in ALL_CHECKS:
+        check(oracle)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mod = _load_mutant(*MUTATIONS[name])
+    caught = []
+    for check in ALL_CHECKS:
+        try:
+            check(mod)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(check.__name__)
+    assert caught, f"mutation '{name}' passed every pin"
