@@ -1,0 +1,141 @@
+"""GQA flash attention for MI355X (gfx950): thin Python binding over libgqafa.so.
+
+Every function below marshals torch tensors into device pointers plus the
+current HIP stream and calls the C ABI (include/gqafa.h). All computation
+runs in the HIP kernels; nothing here falls back to another implementation.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import FAError, check, load  # noqa: F401
+
+__all__ = ["prefill", "decode_paged", "decode_workspace_bytes", "combine_lse",
+           "paged_gather", "FAError", "load"]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t, name, dtype, device=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | None = None,
+            out=None, lse=None, return_lse: bool = True):
+    """q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16 -> (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32)."""
+    B, Sq, Hq, D = q.shape
+    _, Skv, Hkv, _ = k.shape
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, torch.bfloat16, dev)
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    check(load().fa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                            B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), int(window), float(scale),
+                            _stream(dev)))
+    return out, lse
+
+
+def decode_workspace_bytes(B, Sq, Hq, D, max_seq_len, kv_chunk) -> int:
+    return int(load().fa_decode_workspace_bytes(B, Sq, Hq, D, max_seq_len, kv_chunk))
+
+
+def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 16,
+                 kv_chunk: int = 256, causal: bool = True, window: int = 0,
+                 scale: float | None = None, workspace=None, out=None, lse=None,
+                 return_lse: bool = True):
+    """Split-KV decode / verify.
+
+    q [B,Sq,Hq,D] bf16; with block_table (int32 [B, max_pages]) the caches are
+    [num_pages, page_size, Hkv, D]; without it they are contiguous
+    [B, Smax, Hkv, D] (Smax a multiple of page_size). seq_lens int32 [B].
+    """
+    B, Sq, Hq, D = q.shape
+    dev = q.device
+    _require(q, "q", torch.bfloat16, dev)
+    _require(kcache, "kcache", torch.bfloat16, dev)
+    _require(vcache, "vcache", torch.bfloat16, dev)
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    if vcache.shape != kcache.shape:
+        raise ValueError("kcache and vcache differ in shape")
+    Hkv = kcache.shape[2]
+    if block_table is not None:
+        _require(block_table, "block_table", torch.int32, dev)
+        num_pages = kcache.shape[0]
+        if kcache.shape[1] != page_size:
+            raise ValueError("cache page dimension differs from page_size")
+        max_pages = block_table.shape[1]
+    else:
+        num_pages = 0
+        if kcache.shape[1] % page_size:
+            raise ValueError("contiguous cache length must be a multiple of page_size")
+        max_pages = kcache.shape[1] // page_size
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_bytes(B, Sq, Hq, D, max_pages * page_size, kv_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    check(load().fa_decode_paged(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                 _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                 B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
+                                 int(bool(causal)), int(window), float(scale),
+                                 _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, lse
+
+
+def combine_lse(o_part, lse_part, n_chunks=None, *, out=None, lse=None):
+    """o_part fp32 [B,Hq,Sq,C,D], lse_part fp32 [B,Hq,Sq,C] -> (o bf16 [B,Sq,Hq,D], lse [B,Hq,Sq])."""
+    B, Hq, Sq, C, D = o_part.shape
+    dev = o_part.device
+    _require(o_part, "o_part", torch.float32, dev)
+    _require(lse_part, "lse_part", torch.float32, dev)
+    if n_chunks is not None:
+        _require(n_chunks, "n_chunks", torch.int32, dev)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    check(load().fa_combine_lse(_ptr(o_part), _ptr(lse_part), _ptr(n_chunks), C, _ptr(out),
+                                _ptr(lse), B, Sq, Hq, D, _stream(dev)))
+    return out, lse
+
+
+def paged_gather(cache, block_table, seq_lens, *, out=None):
+    """Test hook: dense [B, max_pages*page_size, Hkv, D] copy of a paged cache."""
+    P, ps, Hkv, D = cache.shape
+    B, max_pages = block_table.shape
+    dev = cache.device
+    _require(cache, "cache", torch.bfloat16, dev)
+    _require(block_table, "block_table", torch.int32, dev)
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    if out is None:
+        out = torch.empty((B, max_pages * ps, Hkv, D), dtype=torch.bfloat16, device=dev)
+    check(load().fa_paged_gather(_ptr(cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                 B, Hkv, D, P, ps, max_pages, _stream(dev)))
+    return out

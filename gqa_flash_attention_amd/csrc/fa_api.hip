@@ -1,0 +1,154 @@
+// C ABI: host-side validation and dispatch. Nothing here allocates, frees,
+// synchronizes, prints or aborts; an invalid call launches nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/gqafa.h"
+#include "fa_launch.h"
+
+using namespace gqafa;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+
+int log2_exact(int x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t n_chunks_for(int64_t len, int chunk) { return (len + chunk - 1) / chunk; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+// Upper bound on grid sizes and element counts (all kernels index in 64 bits;
+// this keeps the 1-D grids below 2^31 workgroups).
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported shape (head dim must be 64, 128, 256 or 512; page size a power of two)";
+    case FA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Sq, int Skv, int D,
+               int causal, int window, float scale, void* stream) {
+  if (B < 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return FA_OK;
+  if (!q || !o || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (Skv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)Sq * (Hq / Hkv);
+  if ((int64_t)B * Hkv * ((rows + 127) / 32) > kMaxGrid) return FA_ERR_INVALID_ARG;
+  PrefillDesc d{q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, window, scale};
+  return to_status(launch_prefill(d, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
+  if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0) return 0;
+  const int64_t chunks = n_chunks_for(max_seq_len, kv_chunk);
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  const size_t o_bytes = align256((size_t)(rows * chunks * D) * sizeof(float));
+  const size_t l_bytes = align256((size_t)(rows * chunks) * sizeof(float));
+  return o_bytes + l_bytes;
+}
+
+int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* o, float* lse,
+                    int B, int Sq, int Hq, int Hkv, int D,
+                    int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                    int causal, int window, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (max_pages_per_seq < 0 || kv_chunk <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  const int page_shift = log2_exact(page_size);
+  if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
+  const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
+  if (max_len > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (block_table != nullptr && num_pages <= 0) return FA_ERR_INVALID_ARG;
+  if (B == 0 || Sq == 0) return FA_OK;
+  if (!q || !o || !seq_lens || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (max_len > 0 && (!kcache || !vcache || !aligned16(kcache) || !aligned16(vcache)))
+    return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_workspace_bytes(B, Sq, Hq, D, (int)max_len, kv_chunk);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return FA_ERR_WORKSPACE;
+  const int64_t max_chunks = n_chunks_for(max_len, kv_chunk);
+  const int64_t rows = (int64_t)Sq * (Hq / Hkv);
+  if ((int64_t)B * Hkv * ((rows + 31) / 32) * (max_chunks > 0 ? max_chunks : 1) > kMaxGrid)
+    return FA_ERR_INVALID_ARG;
+
+  const int64_t prow = (int64_t)B * Hq * Sq;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256((size_t)(prow * max_chunks * D) * sizeof(float)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (max_chunks > 0) {
+    SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part,
+                 B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
+                 (int)max_chunks, causal, window, scale};
+    const int s = to_status(launch_split(sd, st));
+    if (s != FA_OK) return s;
+  }
+  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)max_chunks, o, lse, B, Sq, Hq, D};
+  return to_status(launch_combine(cd, st));
+}
+
+int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_chunks,
+                   int max_chunks, void* o, float* lse,
+                   int B, int Sq, int Hq, int D, void* stream) {
+  if (B < 0 || Sq < 0 || Hq <= 0 || max_chunks < 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return FA_OK;
+  if (!o || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (max_chunks > 0 && (!o_part || !lse_part || !aligned16(o_part))) return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  if (((int64_t)B * Hq * Sq + 3) / 4 > kMaxGrid) return FA_ERR_INVALID_ARG;
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, B, Sq, Hq, D};
+  return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
+}
+
+int fa_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,
+                    void* out, int B, int Hkv, int D, int num_pages, int page_size,
+                    int max_pages_per_seq, void* stream) {
+  if (B < 0 || Hkv <= 0 || max_pages_per_seq < 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  const int page_shift = log2_exact(page_size);
+  if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
+  if (((int64_t)max_pages_per_seq << page_shift) > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (B == 0 || max_pages_per_seq == 0) return FA_OK;
+  if (!cache || !block_table || !seq_lens || !out || num_pages <= 0) return FA_ERR_INVALID_ARG;
+  if (!aligned16(cache) || !aligned16(out)) return FA_ERR_INVALID_ARG;
+  GatherDesc d{cache, block_table, seq_lens, out, B, Hkv, D, num_pages, page_shift, max_pages_per_seq};
+  return to_status(launch_gather(d, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,456 @@
+// Flash-attention tile kernel for gfx950: bf16 MFMA with fp32 accumulators,
+// K/V tiles staged through swizzled LDS, online softmax in registers.
+//
+// Method: the streaming-softmax attention of the scalar flash-attention path
+// (llama.cpp PR 28507, Summary) with K/V staged in on-chip memory once per
+// workgroup and reused by all its query rows (same page, Measurements: the
+// gain grows with context depth). Every partial publishes its row (max,
+// rowsum) as an LSE (beellama.cpp PR 149, Overview: whole-tile blocks must
+// publish their meta or the merge drops them). fp32 accumulation of both
+// products follows the same page (fp16 accumulation compounded over depth into
+// a KL-divergence collapse). The XOR swizzle stays inside the row for every
+// head dim (the AstrAI commit log fixed a swizzle mask wider than the chunk
+// count of a row).
+//
+// Layout of the work. For one KV head g of sequence b the "rows" of the
+// problem are the pairs (query position i, query head h in g's group),
+// numbered r = i * G + (h - g * G). Rows of one position are adjacent in
+// memory ([B, Sq, Hq, D]), so a block of 32 rows is a few positions times the
+// whole head group, and every row of a workgroup reads the same K/V tile.
+//
+// Each wave owns 32 rows. It computes S^T = K Q^T for a tile of keys with
+// v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T from registers), so
+// each lane holds the scores of ONE query row for 16 keys of every 32-key
+// block: the row max is an in-lane max plus one exchange with the lane 32
+// away, and the row sum never needs a cross-lane step until the end. The
+// score accumulators, rounded to bf16, are already the B operand of
+// O^T = V^T P^T; V is written to LDS transposed (key-contiguous per d) with
+// bits 2 and 3 of the key index exchanged, so that each lane's eight keys of
+// a K step sit in one 16-byte LDS chunk.
+//
+// D split (DS = 2, used for the large head dims): two waves share the same 32
+// rows; each holds half of Q's head dim and half of O. Each computes the
+// partial S^T over its half of the contraction, the pair adds the two halves
+// through LDS (in the same order in both waves, so both hold bit-identical
+// scores and run identical softmax), and each then accumulates its half of O.
+// K and V tiles are still read from LDS exactly once per row block.
+#pragma once
+
+#include "fa_device.h"
+
+namespace gqafa {
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;            // final output (prefill)
+  float* lse;             // final LSE (prefill), may be null
+  float* o_part;          // split mode: fp32 [B, Hq, Sq, max_chunks, D]
+  float* lse_part;        // split mode: fp32 [B, Hq, Sq, max_chunks]
+  const int32_t* seq_lens;  // split mode: keys per sequence
+  const int32_t* table;     // split mode: block table or null
+  int page_shift, max_pages, num_pages;
+  int64_t slots;          // contiguous layout: token slots per sequence
+  int B, Sq, Hq, Hkv, G;
+  int skv;                // prefill: keys per sequence
+  int causal, window;
+  float sl2;              // scale * log2(e)
+  int n_rb;               // row blocks per (b, g)
+  int chunk, max_chunks;  // split mode
+};
+
+// Spread a 1-D grid over the 8 XCDs so that logical neighbours (row blocks of
+// one (b, KV head), which read the same K/V) share an XCD and its L2.
+// Workgroup i is dispatched to XCD i % 8; this returns the logical index.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  constexpr int X = 8;
+  const int per = n / X, rem = n % X;
+  const int x = i % X, k = i / X;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + k;
+}
+
+// Position inside a 16-key group after exchanging key bits 2 and 3.
+__device__ __forceinline__ int vt_quad_pos(int quad) {
+  return (quad & ~3) | ((quad & 1) << 1) | ((quad >> 1) & 1);
+}
+
+template <int D, int NW, int BN, int DS, bool PAGED, bool SPLIT, bool PREFETCH>
+__global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
+  static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(DS == 1 || (DS == 2 && NW % 2 == 0), "a D split pairs waves");
+  constexpr int T = NW * 64;
+  constexpr int BM = NW * 32 / DS;
+  constexpr int KCH = D / 8;                  // 16-byte chunks per K row
+  constexpr int NBUF = PREFETCH ? 2 : 1;
+  constexpr int K_UNITS = BN * KCH;           // one 16-byte chunk each
+  constexpr int K_PER_T = (K_UNITS + T - 1) / T;
+  constexpr int V_UNITS = (BN / 4) * KCH;     // four keys x eight d each
+  constexpr int V_PER_T = (V_UNITS + T - 1) / T;
+  constexpr int NKB = BN / 32;                // 32-key score blocks per tile
+  constexpr int NKS = BN / 16;                // 16-key steps of the PV product
+  constexpr int NDB = D / 32 / DS;            // 32-wide d blocks of O per wave
+  constexpr int NQC = D / 16 / DS;            // 16-wide d steps of Q K^T per wave
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][D * BN];
+  // partial scores exchanged by the two waves of a D split, [wave][value][lane]
+  __shared__ float sX[DS == 2 ? NW : 1][DS == 2 ? NKB * 16 : 1][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane & 31;     // this lane's query row inside the wave
+  const int hl = lane >> 5;    // lane half
+  const int rg = wave / DS;    // row group (32 rows) of this wave
+  const int dh = wave % DS;    // which half of the head dim this wave holds
+
+  // ---- work item -------------------------------------------------------
+  int b, g, rb, cid = 0;
+  if constexpr (SPLIT) {
+    int L = blockIdx.x;
+    cid = L % a.max_chunks;
+    L /= a.max_chunks;
+    rb = L % a.n_rb;
+    const int bg = L / a.n_rb;
+    b = bg / a.Hkv;
+    g = bg % a.Hkv;
+  } else {
+    const int n = a.B * a.Hkv * a.n_rb;
+    const int L = xcd_remap(blockIdx.x, n);
+    const int bg = L / a.n_rb;
+    rb = a.n_rb - 1 - (L % a.n_rb);   // heaviest causal row blocks first
+    b = bg / a.Hkv;
+    g = bg % a.Hkv;
+  }
+
+  int n_keys;
+  if constexpr (SPLIT) {
+    const int64_t cap = (int64_t)a.max_pages << a.page_shift;
+    int64_t sl = a.seq_lens[b];
+    sl = sl < 0 ? 0 : (sl > cap ? cap : sl);
+    n_keys = (int)sl;
+    if ((int64_t)cid * a.chunk >= n_keys) return;  // past the end: the merge skips it
+  } else {
+    n_keys = a.skv;
+  }
+
+  const int rows = a.Sq * a.G;
+  const int r_lo = rb * BM;
+  const int r_hi = min(r_lo + BM, rows);
+  const int shift = n_keys - a.Sq;             // bottom-right causal alignment
+  const int pmin = r_lo / a.G + shift;
+  const int pmax = (r_hi - 1) / a.G + shift;
+
+  // keys this workgroup may need: [kv_lo, kv_hi), inside the split [kb0, ke)
+  int kb0 = 0, ke = n_keys;
+  if constexpr (SPLIT) {
+    kb0 = cid * a.chunk;
+    ke = min(n_keys, kb0 + a.chunk);
+  }
+  int kv_lo = kb0, kv_hi = ke;
+  if (a.causal) {
+    kv_hi = min(kv_hi, pmax + 1);
+    if (a.window > 0) kv_lo = max(kv_lo, pmin - a.window + 1);
+  }
+  const int t_start = kb0 + ((max(kv_lo, kb0) - kb0) / BN) * BN;
+  const int n_tiles = kv_hi > kv_lo ? (kv_hi - t_start + BN - 1) / BN : 0;
+
+  // ---- this lane's query row ---------------------------------------------
+  const int wr_lo = r_lo + 32 * rg;
+  const bool wave_rows = wr_lo < r_hi;
+  const int wr_hi = min(wr_lo + 32, r_hi);
+  const int wpmin = wr_lo / a.G + shift;
+  const int wpmax = (wr_hi - 1) / a.G + shift;
+  const int r = wr_lo + j;
+  const bool row_ok = r < r_hi;
+  const int qi = row_ok ? r / a.G : 0;
+  const int qh = g * a.G + (row_ok ? r % a.G : 0);
+  const int p = qi + shift;                    // absolute position of the row
+
+  bf16x8 qf[NQC];
+  {
+    const int64_t qoff = (((int64_t)b * a.Sq + qi) * a.Hq + qh) * D + 8 * hl + dh * (D / DS);
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
+      qf[c] = as_bf16x8(w);
+    }
+  }
+
+  // ---- K/V address function ---------------------------------------------
+  KvAddr kv;
+  kv.table = PAGED ? a.table : nullptr;
+  kv.page_shift = a.page_shift;
+  kv.max_pages = a.max_pages;
+  kv.num_pages = a.num_pages;
+  kv.slots = a.slots;
+  kv.row_stride = (int64_t)a.Hkv * D;
+  kv.head_off = (int64_t)g * D;
+
+  // One K unit is a 16-byte chunk of one key row; one V unit is the same
+  // chunk of four consecutive key rows, written to LDS transposed.
+  auto load_k = [&](int tb, int u) -> u32x4 {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (K_UNITS % T == 0 || u < K_UNITS) {
+      const int t = tb + u / KCH;
+      const int64_t off = t < ke ? kv.row(b, t) : -1;
+      if (off >= 0) w = *reinterpret_cast<const u32x4*>(a.k + off + 8 * (u % KCH));
+    }
+    return w;
+  };
+  auto store_k = [&](int buf, int u, const u32x4& w) {
+    if (K_UNITS % T == 0 || u < K_UNITS) {
+      const int key = u / KCH, ch = u % KCH;
+      *reinterpret_cast<u32x4*>(&sK[buf][key * D + 8 * swz_chunk<D * 2>(key, ch)]) = w;
+    }
+  };
+  auto load_v = [&](int tb, int u, u32x4* w4) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (V_UNITS % T == 0 || u < V_UNITS) {
+        const int t = tb + 4 * (u / KCH) + jj;
+        const int64_t off = t < ke ? kv.row(b, t) : -1;
+        if (off >= 0) w = *reinterpret_cast<const u32x4*>(a.v + off + 8 * (u % KCH));
+      }
+      w4[jj] = w;
+    }
+  };
+  auto store_v = [&](int buf, int u, const u32x4* w4) {
+    if (V_UNITS % T == 0 || u < V_UNITS) {
+      const int dc = u % KCH, quad = u / KCH;
+      const int pos = 4 * vt_quad_pos(quad);     // key position inside the row
+      const int chunk = pos >> 3, half = (pos >> 2) & 1;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int w = dd >> 1;
+        uint32_t x01, x23;
+        if ((dd & 1) == 0) {
+          x01 = pack_lo16(w4[0][w], w4[1][w]);
+          x23 = pack_lo16(w4[2][w], w4[3][w]);
+        } else {
+          x01 = pack_hi16(w4[0][w], w4[1][w]);
+          x23 = pack_hi16(w4[2][w], w4[3][w]);
+        }
+        const int d = 8 * dc + dd;
+        u32x2 val = {x01, x23};
+        *reinterpret_cast<u32x2*>(&sV[buf][d * BN + 8 * swz_chunk<BN * 2>(d, chunk) + 4 * half]) = val;
+      }
+    }
+  };
+
+  // Register double buffer for the prefetching variant.
+  u32x4 kreg[PREFETCH ? K_PER_T : 1];
+  u32x4 vreg[PREFETCH ? V_PER_T : 1][4];
+  auto load_tile = [&](int tb) {
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int i = 0; i < K_PER_T; ++i) kreg[i] = load_k(tb, tid + i * T);
+#pragma unroll
+      for (int i = 0; i < V_PER_T; ++i) load_v(tb, tid + i * T, vreg[i]);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int i = 0; i < K_PER_T; ++i) store_k(buf, tid + i * T, kreg[i]);
+#pragma unroll
+      for (int i = 0; i < V_PER_T; ++i) store_v(buf, tid + i * T, vreg[i]);
+    }
+  };
+  // Direct staging in small pieces (bounded register use).
+  auto stage_tile = [&](int tb, int buf) {
+    constexpr int PK = 4;
+#pragma unroll
+    for (int i0 = 0; i0 < K_PER_T; i0 += PK) {
+      u32x4 w[PK];
+#pragma unroll
+      for (int i = 0; i < PK; ++i)
+        if (i0 + i < K_PER_T) w[i] = load_k(tb, tid + (i0 + i) * T);
+#pragma unroll
+      for (int i = 0; i < PK; ++i)
+        if (i0 + i < K_PER_T) store_k(buf, tid + (i0 + i) * T, w[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      u32x4 w4[4];
+      load_v(tb, tid + i * T, w4);
+      store_v(buf, tid + i * T, w4);
+    }
+  };
+
+  // ---- running state -----------------------------------------------------
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float sl2 = a.sl2;
+
+  auto compute_tile = [&](int buf, int tb) {
+    // wave-uniform: skip tiles with no visible key for any row of the wave
+    const bool active = wave_rows && tb < ke && !(a.causal && tb > wpmax) &&
+                        !(a.causal && a.window > 0 && tb + BN - 1 <= wpmin - a.window);
+    if (DS == 1 && !active) return;
+    const bool full = (tb + BN <= ke) && (!a.causal || tb + BN - 1 <= wpmin) &&
+                      (!a.causal || a.window <= 0 || wpmax - tb < a.window);
+
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    if (active) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = 32 * kb + j;
+#pragma unroll
+        for (int c = 0; c < NQC; ++c) {
+          const int ch = 2 * (c + dh * NQC) + hl;
+          const u32x4 kw = *reinterpret_cast<const u32x4*>(
+              &sK[buf][row * D + 8 * swz_chunk<D * 2>(row, ch)]);
+          s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
+        }
+      }
+    }
+    if constexpr (DS == 2) {
+      if (active) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) sX[wave][kb * 16 + x][lane] = s[kb][x];
+      }
+      __syncthreads();
+      if (!active) return;
+      // lower half first in both waves: identical sums in the pair
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const float other = sX[wave ^ 1][kb * 16 + x][lane];
+          s[kb][x] = dh == 0 ? s[kb][x] + other : other + s[kb][x];
+        }
+    }
+
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int key = tb + 32 * kb + 8 * (x >> 2) + 4 * hl + (x & 3);
+          bool vis = key < ke;
+          if (a.causal) {
+            vis = vis && key <= p;
+            if (a.window > 0) vis = vis && (p - key) < a.window;
+          }
+          if (!vis) s[kb][x] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[kb][x]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * sl2);
+    const float nb = -m_use * sl2;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float e = fast_exp2(fmaf(s[kb][x], sl2, nb));
+        s[kb][x] = e;
+        ls += e;
+      }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    u32x4 pf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kb = ks >> 1, base = 8 * (ks & 1);
+      pf[ks][0] = pack_bf16(s[kb][base + 0], s[kb][base + 1]);
+      pf[ks][1] = pack_bf16(s[kb][base + 2], s[kb][base + 3]);
+      pf[ks][2] = pack_bf16(s[kb][base + 4], s[kb][base + 5]);
+      pf[ks][3] = pack_bf16(s[kb][base + 6], s[kb][base + 7]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * (db + dh * NDB) + j;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(
+            &sV[buf][d * BN + 8 * swz_chunk<BN * 2>(d, 2 * ks + hl)]);
+        oacc[db] = mfma32(as_bf16x8(vw), as_bf16x8(pf[ks]), oacc[db]);
+      }
+    }
+  };
+
+  // ---- main loop: one barrier per tile -----------------------------------
+  if constexpr (PREFETCH) {
+    if (n_tiles > 0) {
+      load_tile(t_start);
+      store_tile(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < n_tiles; ++it) {
+      const int tb = t_start + it * BN;
+      const int cur = it & 1;
+      const bool more = it + 1 < n_tiles;
+      if (more) load_tile(tb + BN);
+      compute_tile(cur, tb);
+      if (more) store_tile(cur ^ 1);
+      __syncthreads();
+    }
+  } else {
+    for (int it = 0; it < n_tiles; ++it) {
+      const int tb = t_start + it * BN;
+      stage_tile(tb, 0);
+      __syncthreads();
+      compute_tile(0, tb);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----------------------------------------------------------
+  const float l_tot = l_run + swap_halves(l_run);
+  if (!row_ok) return;
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : fast_rcp(l_tot);
+  const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
+
+  if constexpr (SPLIT) {
+    const int64_t prow = (((int64_t)b * a.Hq + qh) * a.Sq + qi) * a.max_chunks + cid;
+    float* dst = a.o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
+        f32x4 val = {oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv,
+                     oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst + d0) = val;
+      }
+    if (hl == 0 && dh == 0) a.lse_part[prow] = lse_v;
+  } else {
+    uint16_t* dst = a.o + (((int64_t)b * a.Sq + qi) * a.Hq + qh) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
+        u32x2 val = {pack_bf16(oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv),
+                     pack_bf16(oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + d0) = val;
+      }
+    if (a.lse != nullptr && hl == 0 && dh == 0) a.lse[((int64_t)b * a.Hq + qh) * a.Sq + qi] = lse_v;
+  }
+}
+
+}  // namespace gqafa

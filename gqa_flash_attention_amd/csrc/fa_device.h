@@ -1,0 +1,95 @@
+// Device helpers for the gfx950 (CDNA4) attention kernels: MFMA operand
+// types, lane exchanges, bf16 packing, LDS swizzles and the KV-cache address
+// function shared by the split-KV kernel and the paged-gather test hook.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqafa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D[32x32] += A[32x16] * B[16x32], bf16 inputs, fp32 accumulators. Lane l
+// supplies row (l % 32) of A and column (l % 32) of B, eight consecutive K
+// slots each; the lane halves (l / 32) hold the two halves of the 16 K slots.
+// Both operands use the same K-slot assignment, so the contraction is the
+// plain sum over the 16 K positions whatever order the unit walks them in.
+// The result layout: acc[4 * r + e] of lane l is D[8 r + 4 (l / 32) + e][l % 32].
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Exchange a value with the lane 32 positions away (v_permlane32_swap).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+// Two fp32 values -> packed bf16 pair (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Low or high 16-bit halves of two words, packed (x half in the low 16 bits).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// 16-byte-chunk XOR swizzle for an LDS tile whose rows are ROW_BYTES long.
+// The 64 four-byte banks repeat every 256 bytes; the XOR spreads sixteen
+// consecutive rows read at the same logical chunk over sixteen distinct
+// 16-byte bank groups. The XOR value stays below the chunk count of a row, so
+// a swizzled chunk never leaves its row.
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+  constexpr int kRowsPer256 = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
+  constexpr int kSpan = 16 / kRowsPer256;
+  static_assert(ROW_BYTES % 16 == 0 && ROW_BYTES >= 64, "row must hold at least four chunks");
+  static_assert(kSpan <= ROW_BYTES / 16, "swizzle must stay inside the row");
+  return chunk ^ ((row / kRowsPer256) % kSpan);
+}
+
+// Element offset of K/V row (sequence b, token t, KV head g) in a cache laid
+// out as pages [num_pages, page_size, Hkv, D] reached through block_table
+// [B, max_pages], or, with no table, as a contiguous [B, slots, Hkv, D]
+// tensor (the identity table). Returns -1 when the table entry is outside
+// [0, num_pages). All arithmetic is 64-bit.
+struct KvAddr {
+  const int32_t* table;   // may be null
+  int page_shift;         // log2(page_size)
+  int max_pages;          // table row length
+  int num_pages;
+  int64_t slots;          // contiguous layout: token slots per sequence
+  int64_t row_stride;     // Hkv * D elements between consecutive tokens
+  int64_t head_off;       // g * D
+
+  __device__ __forceinline__ int64_t row(int b, int t) const {
+    if (table == nullptr) return ((int64_t)b * slots + t) * row_stride + head_off;
+    const int page = table[(int64_t)b * max_pages + (t >> page_shift)];
+    if (page < 0 || page >= num_pages) return -1;
+    const int slot = t & ((1 << page_shift) - 1);
+    return (((int64_t)page << page_shift) + slot) * row_stride + head_off;
+  }
+};
+
+}  // namespace gqafa

@@ -1,0 +1,54 @@
+// Prefill launcher: one workgroup per (sequence, KV head, block of rows).
+#include "fa_attn_kernel.h"
+#include "fa_launch.h"
+
+namespace gqafa {
+
+namespace {
+
+// Tile shape per head dim: waves per workgroup, keys per tile, D split (two
+// waves per 32 rows), and whether the next tile is prefetched into registers
+// while the current one computes.
+template <int D> struct PrefillCfg;
+template <> struct PrefillCfg<64>  { static constexpr int NW = 4, BN = 64, DS = 1; static constexpr bool PF = true; };
+template <> struct PrefillCfg<128> { static constexpr int NW = 4, BN = 64, DS = 1; static constexpr bool PF = true; };
+template <> struct PrefillCfg<256> { static constexpr int NW = 4, BN = 32, DS = 1; static constexpr bool PF = true; };
+template <> struct PrefillCfg<512> { static constexpr int NW = 4, BN = 32, DS = 2; static constexpr bool PF = false; };
+
+template <int D>
+hipError_t run(const PrefillDesc& d, hipStream_t stream) {
+  using C = PrefillCfg<D>;
+  constexpr int BM = C::NW * 32 / C::DS;
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(d.q);
+  a.k = static_cast<const uint16_t*>(d.k);
+  a.v = static_cast<const uint16_t*>(d.v);
+  a.o = static_cast<uint16_t*>(d.o);
+  a.lse = d.lse;
+  a.slots = d.Skv;
+  a.B = d.B; a.Sq = d.Sq; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.Hq / d.Hkv;
+  a.skv = d.Skv;
+  a.causal = d.causal; a.window = d.window;
+  a.sl2 = d.scale * kLog2e;
+  const int64_t rows = (int64_t)d.Sq * a.G;
+  a.n_rb = (int)((rows + BM - 1) / BM);
+  const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, false, false, C::PF>), dim3((unsigned)grid),
+                     dim3(C::NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillDesc& d, hipStream_t stream) {
+  switch (d.D) {
+    case 64: return run<64>(d, stream);
+    case 128: return run<128>(d, stream);
+    case 256: return run<256>(d, stream);
+    case 512: return run<512>(d, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gqafa

@@ -1,0 +1,151 @@
+/*
+ * gqafa.h - C ABI of the MI355X (gfx950) GQA flash-attention library.
+ *
+ * The library computes scaled-dot-product attention, softmax(Q K^T * scale +
+ * mask) V, with a streaming (online) softmax over K/V tiles, for grouped-query
+ * heads, causal and sliding-window masks and head dims 64, 128, 256 and 512.
+ * The computation is the "scalar flash-attention path" of llama.cpp PR 28507
+ * (Vulkan K/V shared-memory staging on AMD RDNA, section Summary), whose SWA
+ * layers use head size 256 and global layers 512 (section Measurements); the
+ * split-KV partials publish a per-row (max, rowsum) pair that a combine step
+ * merges (beellama.cpp PR 149, Make KVarN usable on ROCm RDNA3, section
+ * Overview and the first review).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned, owned by the
+ *     caller. The library never allocates, frees or synchronizes, and keeps
+ *     no state between calls.
+ *   - bf16 tensors are passed as raw 16-bit storage (bfloat16 bit patterns).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream). Results are ready when the stream reaches the call.
+ *   - Arguments are validated on the host before anything is launched. An
+ *     invalid call returns a negative status and launches nothing. The
+ *     library never aborts and never prints.
+ *   - Query head h reads KV head h / (Hq / Hkv) (consecutive query heads
+ *     share a KV head).
+ *   - Causal masking is bottom-right aligned: query row i of a sequence with
+ *     n keys sits at position i + n - Sq and sees keys j <= that position.
+ *     With window > 0 it only sees keys with position - j < window (exactly
+ *     `window` keys ending at the diagonal). window > 0 requires causal.
+ *   - LSE is the natural log of sum_j exp(scale * q . k_j) over the visible
+ *     keys, in fp32. A row with no visible key gets O = 0 and LSE = -inf.
+ *   - Arithmetic: bf16 inputs, fp32 accumulation of Q K^T and P V, fp32
+ *     softmax state, P rounded to bf16 as the second product's operand.
+ */
+#ifndef GQAFA_H
+#define GQAFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad mask or scale, misaligned pointer */
+  FA_ERR_UNSUPPORTED = -2,  /* head dim not in {64,128,256,512}, page size not a power of two */
+  FA_ERR_WORKSPACE = -3,    /* decode workspace missing or smaller than fa_decode_workspace_bytes */
+  FA_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch */
+} fa_status;
+
+/*
+ * Prefill attention (many query rows per sequence).
+ *
+ *   q   bf16 [B, Sq, Hq, D]   contiguous
+ *   k   bf16 [B, Skv, Hkv, D] contiguous
+ *   v   bf16 [B, Skv, Hkv, D] contiguous
+ *   o   bf16 [B, Sq, Hq, D]   output (round-to-nearest-even)
+ *   lse fp32 [B, Hq, Sq]      output, may be NULL (not written)
+ *
+ * B, Sq, Skv >= 0 (an empty batch or Sq = 0 writes nothing; Skv = 0 gives
+ * O = 0 and LSE = -inf); Hq, Hkv > 0 with Hq % Hkv == 0; D in
+ * {64,128,256,512}; causal 0/1; window >= 0; scale finite and > 0.
+ */
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Sq, int Skv, int D,
+               int causal, int window, float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
+ * [B, Hq, Sq, n_chunks, D] and their LSEs [B, Hq, Sq, n_chunks], with
+ * n_chunks = ceil(max_seq_len / kv_chunk), each region 256-byte aligned.
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk);
+
+/*
+ * Decode (Sq = 1) and speculative verify (a few query rows, causal among
+ * them) over a paged KV cache, split over the KV sequence in chunks of
+ * kv_chunk tokens and merged by LSE (split-KV, "parallel blocks" + combine).
+ *
+ *   q           bf16 [B, Sq, Hq, D]: the Sq newest rows of each sequence
+ *   kcache      bf16 [num_pages, page_size, Hkv, D] when block_table != NULL;
+ *   vcache           bf16 [B, max_pages_per_seq * page_size, Hkv, D] (a
+ *                    contiguous cache, i.e. the identity table) when NULL
+ *   block_table int32 [B, max_pages_per_seq]: token t of sequence b is in
+ *               physical page block_table[b][t / page_size], slot
+ *               t % page_size. May be NULL (contiguous cache).
+ *   seq_lens    int32 [B] on the device: tokens in each sequence's cache,
+ *               including the Sq query rows' own keys; values are clamped to
+ *               [0, max_pages_per_seq * page_size].
+ *   o           bf16 [B, Sq, Hq, D] output
+ *   lse         fp32 [B, Hq, Sq] output, may be NULL
+ *   num_pages   physical pages in the cache (block_table entries outside
+ *               [0, num_pages) are read as masked keys, never dereferenced);
+ *               ignored when block_table is NULL
+ *   page_size   a power of two in [1, 65536]
+ *   kv_chunk    tokens per split, > 0
+ *   workspace   device buffer of at least
+ *               fa_decode_workspace_bytes(B, Sq, Hq, D, max_pages_per_seq*page_size, kv_chunk)
+ *
+ * Two kernels run on `stream`: the split kernel writes partials into the
+ * workspace, then the combine kernel writes o and lse. Calls that share a
+ * workspace must be ordered on one stream.
+ */
+int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* o, float* lse,
+                    int B, int Sq, int Hq, int Hkv, int D,
+                    int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                    int causal, int window, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge split-KV partials by their LSE:
+ *   M = max_c LSE_c,  LSE = M + ln sum_c exp(LSE_c - M),
+ *   O = sum_c exp(LSE_c - LSE) * O_c.
+ * Chunks with LSE_c = -inf have weight 0; a row whose chunks are all empty
+ * gets O = 0, LSE = -inf.
+ *
+ *   o_part   fp32 [B, Hq, Sq, max_chunks, D] (each normalised by its own sum)
+ *   lse_part fp32 [B, Hq, Sq, max_chunks]
+ *   n_chunks int32 [B] on the device: leading chunks of sequence b to merge
+ *            (clamped to [0, max_chunks]); NULL merges all max_chunks
+ *   o        bf16 [B, Sq, Hq, D] output
+ *   lse      fp32 [B, Hq, Sq] output, may be NULL
+ */
+int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_chunks,
+                   int max_chunks, void* o, float* lse,
+                   int B, int Sq, int Hq, int D, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Test hook: gathers a paged cache into a dense tensor with the same device
+ * address function the decode kernel uses.
+ *   cache [num_pages, page_size, Hkv, D] bf16 -> out [B, max_pages_per_seq*page_size, Hkv, D]
+ * Slots at or beyond seq_lens[b], and slots whose table entry is outside
+ * [0, num_pages), are written as zero.
+ */
+int fa_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,
+                    void* out, int B, int Hkv, int D, int num_pages, int page_size,
+                    int max_pages_per_seq, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQAFA_H */

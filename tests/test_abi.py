@@ -1,0 +1,142 @@
+"""The C-ABI library loads, exports every symbol include/gqafa.h declares,
+and rejects invalid calls on the host before any launch (no GPU needed: the
+validation paths return before touching the device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_flash_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqafa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(["fa_prefill", "fa_decode_workspace_bytes", "fa_decode_paged",
+                            "fa_combine_lse", "fa_status_string", "fa_paged_gather"])
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 12345):
+        assert lib.fa_status_string(s)
+
+
+# a fake, 16-byte aligned "device" address: validation must fail before any use
+P = 0x10000
+
+
+def _prefill(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Skv=8, D=128,
+             causal=1, window=0, scale=0.125)
+    a.update(kw)
+    return lib.fa_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Skv"], a["D"], a["causal"], a["window"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=96), UNSUPPORTED), (dict(D=32), UNSUPPORTED), (dict(D=576), UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(B=-1), INVALID), (dict(Sq=-1), INVALID), (dict(Skv=-2), INVALID),
+    (dict(window=4, causal=0), INVALID), (dict(window=-1), INVALID), (dict(causal=2), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(k=None), INVALID),
+    (dict(q=P + 2), INVALID), (dict(v=P + 8), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(B=0), OK), (dict(Sq=0), OK),
+])
+def test_prefill_validation(lib, kw, want):
+    assert _prefill(lib, **kw) == want
+
+
+def _decode(lib, **kw):
+    a = dict(q=P, k=P, v=P, table=P, lens=P, o=P, lse=P, B=2, Sq=1, Hq=8, Hkv=2, D=128,
+             num_pages=64, page_size=16, max_pages=8, chunk=64, causal=1, window=0, scale=0.1,
+             ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.fa_decode_paged(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["lse"],
+                               a["B"], a["Sq"], a["Hq"], a["Hkv"], a["D"], a["num_pages"],
+                               a["page_size"], a["max_pages"], a["chunk"], a["causal"], a["window"],
+                               a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=80), UNSUPPORTED), (dict(page_size=12), UNSUPPORTED), (dict(page_size=0), UNSUPPORTED),
+    (dict(page_size=1 << 17), UNSUPPORTED),
+    (dict(Hq=7), INVALID), (dict(chunk=0), INVALID), (dict(max_pages=-1), INVALID),
+    (dict(window=3, causal=0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(num_pages=0), INVALID), (dict(lens=None), INVALID), (dict(q=None), INVALID),
+    (dict(k=P + 4), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=P + 4), WORKSPACE),
+    (dict(max_pages=1 << 27, page_size=1 << 8), INVALID),
+    (dict(B=0), OK), (dict(Sq=0), OK),
+])
+def test_decode_validation(lib, kw, want):
+    assert _decode(lib, **kw) == want
+
+
+def test_workspace_bytes(lib):
+    f = lib.fa_decode_workspace_bytes
+    # C3 shape: 16 x 32 rows x 64 chunks x (128 + 1) fp32
+    assert f(16, 1, 32, 128, 16384, 256) == 16 * 32 * 64 * 128 * 4 + 16 * 32 * 64 * 4
+    assert f(1, 1, 1, 96, 10, 4) == 0          # unsupported head dim
+    assert f(1, 1, 1, 64, 10, 0) == 0          # bad chunk
+
+
+def test_workspace_bytes_alignment(lib):
+    f = lib.fa_decode_workspace_bytes
+    rows, chunks, D = 1 * 2 * 3, 3, 64
+    o = rows * chunks * D * 4
+    l = rows * chunks * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert f(1, 3, 2, 64, 10, 4) == up(o) + up(l)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=48), UNSUPPORTED), (dict(B=-1), INVALID), (dict(max_chunks=-1), INVALID),
+    (dict(o=None), INVALID), (dict(o_part=None), INVALID), (dict(B=0), OK),
+])
+def test_combine_validation(lib, kw, want):
+    a = dict(o_part=P, lse_part=P, n=None, max_chunks=4, o=P, lse=P, B=1, Sq=1, Hq=2, D=64)
+    a.update(kw)
+    st = lib.fa_combine_lse(a["o_part"], a["lse_part"], a["n"], a["max_chunks"], a["o"], a["lse"],
+                            a["B"], a["Sq"], a["Hq"], a["D"], None)
+    assert st == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=40), UNSUPPORTED), (dict(page_size=3), UNSUPPORTED), (dict(table=None), INVALID),
+    (dict(num_pages=0), INVALID), (dict(out=P + 2), INVALID), (dict(B=0), OK),
+])
+def test_gather_validation(lib, kw, want):
+    a = dict(cache=P, table=P, lens=P, out=P, B=1, Hkv=1, D=64, num_pages=4, page_size=16, max_pages=4)
+    a.update(kw)
+    st = lib.fa_paged_gather(a["cache"], a["table"], a["lens"], a["out"], a["B"], a["Hkv"], a["D"],
+                             a["num_pages"], a["page_size"], a["max_pages"], None)
+    assert st == want
