@@ -352,7 +352,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[kb][x]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = pair_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2((m_run - m_use) * sl2);
@@ -419,7 +419,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
   }
 
   // ---- epilogue ----------------------------------------------------------
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   if (!row_ok) return;
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : fast_rcp(l_tot);

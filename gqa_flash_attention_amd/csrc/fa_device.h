@@ -31,10 +31,19 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Exchange a value with the lane 32 positions away (v_permlane32_swap).
-__device__ __forceinline__ float swap_halves(float x) {
+// Reductions over the two lanes 32 apart (l and l ^ 32), via
+// v_permlane32_swap. With x in both operands, the swap leaves lanes 0-31 with
+// (own, partner) and lanes 32-63 with (partner, own) in its two results, so
+// the max and the sum of the two results are the pair's max and sum in every
+// lane; the sum is formed in the same order (lower lane first) in both
+// halves, so the pair holds bit-identical values.
+__device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Two fp32 values -> packed bf16 pair (round to nearest even), low half first.
