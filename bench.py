@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA flash-attention hot path on one MI355X.
+
+Headline (the JSON line's `value`): causal GQA prefill, B=2, Hq=32, Hkv=8,
+Sq=Skv=4096, D=128, bf16 inputs with fp32 accumulation, in algorithmic
+TFLOP/s (4*D flop per visible (query, key) pair per query head). One step is
+one fa_prefill call over the whole batch; inputs are resident in HBM before
+the timed region starts.
+
+The same line also carries the decode half of the metric (KV-read GB/s):
+  decode: B=16, one query row, Hq=32, Hkv=8, D=128, contiguous KV, lengths
+          uniform in [1024, 16384], 256-token split + LSE combine
+  verify: B=4 x 8 query rows, Hq=64, Hkv=8, D=128, 16-token pages, 32768
+          tokens per sequence, randomly permuted block table
+each timed per call with the L2 / Infinity Cache flushed before the call,
+as algorithmic bytes (K and V of every visible token read once per KV head,
+plus Q, O, LSE, lengths and block table) over the call's duration.
+
+`roofline` describes the prefill kernel: achieved = algorithmic flop per
+launch / mean launch duration measured with HIP events on the launch
+stream, against the bf16 dense MFMA peak. `traffic` comes from the committed
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary when it was taken on the current
+kernel sources, else null. `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (prefill) + KV-read GB/s (decode), % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_c2.txt")
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "gqa_flash_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(Sq: int, Skv: int, causal: bool, window: int, rows=None) -> int:
+    """Number of visible (query row, key) pairs for one query head."""
+    import numpy as np
+
+    i = np.arange(Sq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if not causal:
+        return int(i.size * Skv)
+    p = i + (Skv - Sq)
+    hi = np.minimum(Skv - 1, p)
+    lo = np.maximum(0, p - window + 1) if window > 0 else np.zeros_like(p)
+    return int(np.clip(hi - lo + 1, 0, None).sum())
+
+
+def prefill_flops(s, rows=None, batches=None) -> int:
+    B = s.B if batches is None else batches
+    return 4 * s.D * s.Hq * B * visible_pairs(s.Sq, s.Skv, s.causal, s.window, rows)
+
+
+def decode_bytes(s, lens) -> int:
+    kv = 0
+    for n in lens:
+        n = int(n)
+        # every visible key of the sequence, once per KV head, K and V
+        kv += n * s.Hkv * s.D * 2 * 2
+    q_o = 2 * s.B * s.Sq * s.Hq * s.D * 2
+    lse = s.B * s.Hq * s.Sq * 4
+    meta = s.B * 4 + (s.B * (s.max_len // s.page_size) * 4 if s.page_size else 0)
+    return kv + q_o + lse + meta
+
+
+def read_traffic(src_hash: str):
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src_hash:
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Flusher:
+    """Writes a buffer larger than the Infinity Cache to evict cached K/V."""
+
+    def __init__(self, torch, dev, mib=1024):
+        self.buf = torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def time_calls(torch, fn, steps, flush=None):
+    """Per-call durations (ms) from HIP events on the current stream, plus the
+    event time across all calls and the host wall time."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_all0.record()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = [a.elapsed_time(b) for a, b in ev]
+    return per, t_all0.elapsed_time(t_all1), wall
+
+
+def bench_prefill(torch, fa, workloads, dev, steps, warmup):
+    s = workloads.C2
+    q, k, v = workloads.prefill_inputs(s)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((s.B, s.Hq, s.Sq), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.prefill(q, k, v, causal=True, scale=s.scale, out=o, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    per, total_ms, wall = time_calls(torch, step, steps)
+    flops = prefill_flops(s)
+    ms_step = total_ms / steps
+    launch_ms = sum(per) / len(per)
+    return dict(shape=s, flops=flops, ms_per_step=ms_step, launch_ms=launch_ms,
+                tflops=flops / (ms_step * 1e-3) / 1e12,
+                launch_tflops=flops / (launch_ms * 1e-3) / 1e12, wall_s=wall, inputs=(q, k, v))
+
+
+def bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush):
+    di = workloads.decode_inputs(shape)
+    q = di.q.to(dev)
+    kc, vc = di.kcache.to(dev), di.vcache.to(dev)
+    table = None if di.block_table is None else di.block_table.to(dev)
+    lens = di.seq_lens.to(dev)
+    ps = shape.page_size or 16
+    max_pages = (di.block_table.shape[1] if table is not None else shape.max_len // ps)
+    ws = torch.empty(fa.decode_workspace_bytes(shape.B, shape.Sq, shape.Hq, shape.D,
+                                               max_pages * ps, shape.kv_chunk),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((shape.B, shape.Hq, shape.Sq), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.decode_paged(q, kc, vc, table, lens, page_size=ps, kv_chunk=shape.kv_chunk,
+                        causal=True, scale=shape.scale, workspace=ws, out=o, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    per, _, _ = time_calls(torch, step, steps, flush=flush)
+    nbytes = decode_bytes(shape, di.seq_lens.tolist())
+    ms = sorted(per)[len(per) // 2]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": shape.name, "ms_per_call_median": round(ms, 4),
+            "algorithmic_bytes": nbytes, "GB_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "kv_chunk": shape.kv_chunk, "cache": "flushed before each call (1 GiB write)",
+            "sum_seq_len": int(di.seq_lens.sum())}
+
+
+def cpu_baseline(workloads, inputs_cpu):
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    s = workloads.C2
+    q, k, v = inputs_cpu
+    budget_s = 12.0
+    block = 256
+    done_rows = 0
+    flops = 0
+    t0 = time.perf_counter()
+    # blocks of query rows (all heads) of sequence 0, then 1, spread over the
+    # sequence so the sample has the workload's mix of short and long causal rows
+    nblk = s.Sq // block
+    order = [(b, (i * 5) % nblk) for b in range(s.B) for i in range(nblk)]
+    for b, blk in order:
+        rows = np.arange(blk * block, (blk + 1) * block)
+        oracle.attention_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=True, scale=s.scale, rows=rows)
+        done_rows += rows.size
+        flops += prefill_flops(s, rows=rows, batches=1)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"all 32 query heads, {done_rows} of {s.B * s.Sq} query rows (both sequences) in "
+                      f"blocks of {block} ({flops / 1e9:.1f} algorithmic GFLOP), fp64 numpy, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode and verify legs")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels run on a single MI355X; see the sharding notes in the design document).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gqa_flash_attention_amd as fa
+    import workloads
+
+    if not os.path.exists(os.path.join(ROOT, "gqa_flash_attention_amd", "libgqafa.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    pre = bench_prefill(torch, fa, workloads, dev, args.steps, args.warmup)
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash)
+    achieved = pre["launch_tflops"]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "attn_kernel<D=128> (fa_prefill)",
+                "flop_per_launch": pre["flops"], "launch_ms_mean": round(pre["launch_ms"], 4),
+                "source_hash": src_hash}
+
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16)",
+        "config": {"workload": "GQA causal prefill B=2 Hq=32 Hkv=8 Sq=Skv=4096 D=128",
+                   "global_batch": 2, "seq_len": 4096, "Hq": 32, "Hkv": 8, "D": 128,
+                   "causal": True, "scale": "1/sqrt(128)", "parallelism": "single GPU"},
+        "frac_of_peak": round(pre["tflops"] / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+    }
+    q, k, v = pre.pop("inputs")
+    del q, k, v
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        flush = Flusher(torch, dev)
+        dec = bench_decode(torch, fa, workloads, dev, workloads.C3, args.steps, args.warmup, flush)
+        torch.cuda.empty_cache()
+        ver = bench_decode(torch, fa, workloads, dev, workloads.C5, args.steps, args.warmup, flush)
+        line["decode"] = dec
+        line["verify"] = ver
+        del flush
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(workloads, workloads.prefill_inputs(workloads.C2))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
