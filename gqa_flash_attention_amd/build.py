@@ -31,6 +31,10 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the softmax rescales them with
+    # VALU ops, which cannot address AGPRs (AGPR accumulators cost a copy in
+    # and out for every rescale)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

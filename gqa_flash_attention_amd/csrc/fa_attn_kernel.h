@@ -75,8 +75,8 @@ __device__ __forceinline__ int vt_quad_pos(int quad) {
   return (quad & ~3) | ((quad & 1) << 1) | ((quad >> 1) & 1);
 }
 
-template <int D, int NW, int BN, int DS, bool PAGED, bool SPLIT, bool PREFETCH>
-__global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
+template <int D, int NW, int BN, int DS, bool PAGED, bool SPLIT, bool PREFETCH, int WPE>
+__global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert(DS == 1 || (DS == 2 && NW % 2 == 0), "a D split pairs waves");
   constexpr int T = NW * 64;
@@ -180,23 +180,32 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
   }
 
   // ---- K/V address function ---------------------------------------------
-  KvAddr kv;
-  kv.table = PAGED ? a.table : nullptr;
-  kv.page_shift = a.page_shift;
-  kv.max_pages = a.max_pages;
-  kv.num_pages = a.num_pages;
-  kv.slots = a.slots;
-  kv.row_stride = (int64_t)a.Hkv * D;
-  kv.head_off = (int64_t)g * D;
+  // Element offset of key t's row (KV head g). Callers clamp t into the
+  // sequence, and a block-table entry outside [0, num_pages) is clamped into
+  // range: every load stays inside the cache, so no load needs a guard.
+  const int64_t row_stride = (int64_t)a.Hkv * D;
+  const int64_t head_off = (int64_t)g * D;
+  auto key_off = [&](int t) -> int64_t {
+    if constexpr (PAGED) {
+      int page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
+      page = min(max(page, 0), a.num_pages - 1);
+      const int64_t slot = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+      return slot * row_stride + head_off;
+    } else {
+      return ((int64_t)b * a.slots + t) * row_stride + head_off;
+    }
+  };
 
   // One K unit is a 16-byte chunk of one key row; one V unit is the same
   // chunk of four consecutive key rows, written to LDS transposed.
+  // Keys past the end of the range are clamped onto its last key: their
+  // scores are masked and their V rows get weight exactly 0, so the data
+  // read there never matters (and is always finite in-range data).
   auto load_k = [&](int tb, int u) -> u32x4 {
     u32x4 w = {0u, 0u, 0u, 0u};
     if (K_UNITS % T == 0 || u < K_UNITS) {
-      const int t = tb + u / KCH;
-      const int64_t off = t < ke ? kv.row(b, t) : -1;
-      if (off >= 0) w = *reinterpret_cast<const u32x4*>(a.k + off + 8 * (u % KCH));
+      const int t = min(tb + u / KCH, ke - 1);
+      w = *reinterpret_cast<const u32x4*>(a.k + key_off(t) + 8 * (u % KCH));
     }
     return w;
   };
@@ -211,9 +220,8 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
     for (int jj = 0; jj < 4; ++jj) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (V_UNITS % T == 0 || u < V_UNITS) {
-        const int t = tb + 4 * (u / KCH) + jj;
-        const int64_t off = t < ke ? kv.row(b, t) : -1;
-        if (off >= 0) w = *reinterpret_cast<const u32x4*>(a.v + off + 8 * (u % KCH));
+        const int t = min(tb + 4 * (u / KCH) + jj, ke - 1);
+        w = *reinterpret_cast<const u32x4*>(a.v + key_off(t) + 8 * (u % KCH));
       }
       w4[jj] = w;
     }
@@ -285,9 +293,10 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;   // reference max of the row (raw score units)
+  float l_run = 0.f;         // this lane's part of the row sum
   const float sl2 = a.sl2;
+  const float thr = kRescaleLog2 / sl2;
 
   auto compute_tile = [&](int buf, int tb) {
     // wave-uniform: skip tiles with no visible key for any row of the wave
@@ -333,17 +342,17 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
     }
 
     if (!full) {
+      // visible iff lo_lim <= key - tb - 4*hl <= hi_lim; the left side is a
+      // per-element constant
+      const int base = tb + 4 * hl;
+      const int hi_lim = min(ke - 1, a.causal ? p : INT_MAX) - base;
+      const int lo_lim = (a.causal && a.window > 0) ? p - a.window + 1 - base : INT_MIN;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int key = tb + 32 * kb + 8 * (x >> 2) + 4 * hl + (x & 3);
-          bool vis = key < ke;
-          if (a.causal) {
-            vis = vis && key <= p;
-            if (a.window > 0) vis = vis && (p - key) < a.window;
-          }
-          if (!vis) s[kb][x] = -INFINITY;
+          const int rel = 32 * kb + 8 * (x >> 2) + (x & 3);
+          s[kb][x] = (rel <= hi_lim && rel >= lo_lim) ? s[kb][x] : -INFINITY;
         }
     }
 
@@ -353,33 +362,38 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[kb][x]);
     mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * sl2);
-    const float nb = -m_use * sl2;
-    float ls = 0.f;
+    // Lazy rescale: the running reference max only moves when a row's max
+    // grows by more than kRescaleLog2 in the exponent. exp(s - m_ref) then
+    // stays below 2^kRescaleLog2, the final O / l and LSE are unchanged,
+    // and most tiles skip the O rescale entirely (wave-uniform branch).
+    const bool grow = mx > m_run + thr;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2((m_run - m_new) * sl2) : 1.0f;
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float e = fast_exp2(fmaf(s[kb][x], sl2, nb));
-        s[kb][x] = e;
-        ls += e;
-      }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
 
+    // P = exp2(s*c - m*c) as bf16 pairs: already the B operand of O^T += V^T P^T.
+    // The row sum adds the fp32 values: with few visible keys, summing the
+    // bf16-rounded P would put bf16's 2^-9 relative error straight into LSE.
     u32x4 pf[NKS];
+    float ls = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kb = ks >> 1, base = 8 * (ks & 1);
-      pf[ks][0] = pack_bf16(s[kb][base + 0], s[kb][base + 1]);
-      pf[ks][1] = pack_bf16(s[kb][base + 2], s[kb][base + 3]);
-      pf[ks][2] = pack_bf16(s[kb][base + 4], s[kb][base + 5]);
-      pf[ks][3] = pack_bf16(s[kb][base + 6], s[kb][base + 7]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float e0 = fast_exp2(fmaf(s[kb][base + 2 * w], sl2, nb));
+        const float e1 = fast_exp2(fmaf(s[kb][base + 2 * w + 1], sl2, nb));
+        ls += e0 + e1;
+        pf[ks][w] = pack_bf16(e0, e1);
+      }
     }
+    l_run += ls;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = 32 * (db + dh * NDB) + j;

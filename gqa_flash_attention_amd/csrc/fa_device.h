@@ -18,6 +18,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The online softmax moves its reference max only when a row's max grows by
+// more than this many powers of two (P then stays below 2^8).
+constexpr float kRescaleLog2 = 8.0f;
 
 // D[32x32] += A[32x16] * B[16x32], bf16 inputs, fp32 accumulators. Lane l
 // supplies row (l % 32) of A and column (l % 32) of B, eight consecutive K
