@@ -1,5 +1,6 @@
 // Flash-attention tile kernel for gfx950: bf16 MFMA with fp32 accumulators,
-// K/V tiles staged through swizzled LDS, online softmax in registers.
+// K/V tiles streamed into swizzled LDS by direct global->LDS loads, online
+// softmax in registers.
 //
 // Method: the streaming-softmax attention of the scalar flash-attention path
 // (llama.cpp PR 28507, Summary) with K/V staged in on-chip memory once per
@@ -8,7 +9,7 @@
 // rowsum) as an LSE (beellama.cpp PR 149, Overview: whole-tile blocks must
 // publish their meta or the merge drops them). fp32 accumulation of both
 // products follows the same page (fp16 accumulation compounded over depth into
-// a KL-divergence collapse). The XOR swizzle stays inside the row for every
+// a KL-divergence collapse). Every XOR swizzle stays inside its row for every
 // head dim (the AstrAI commit log fixed a swizzle mask wider than the chunk
 // count of a row).
 //
@@ -22,18 +23,23 @@
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T from registers), so
 // each lane holds the scores of ONE query row for 16 keys of every 32-key
 // block: the row max is an in-lane max plus one exchange with the lane 32
-// away, and the row sum never needs a cross-lane step until the end. The
-// score accumulators, rounded to bf16, are already the B operand of
-// O^T = V^T P^T; V is written to LDS transposed (key-contiguous per d) with
-// bits 2 and 3 of the key index exchanged, so that each lane's eight keys of
-// a K step sit in one 16-byte LDS chunk.
+// away, and the row sum needs no cross-lane step until the end. The score
+// accumulators, rounded to bf16, are already the B operand of O^T = V^T P^T;
+// the V^T operand comes straight from the row-major V tile through the
+// transposing LDS read ds_read_b64_tr_b16.
+//
+// Staging. K and V tiles are copied by global_load_lds_dwordx4: each lane's
+// 16-byte load lands at (segment base + 16 * lane) in LDS, so a swizzled LDS
+// layout is produced by choosing WHICH global chunk each lane fetches. Two
+// LDS buffers per operand (separate objects) let the loads of tile t+1 run
+// while tile t is computed, with one barrier per tile; no registers hold the
+// tile in flight.
 //
 // D split (DS = 2, used for the large head dims): two waves share the same 32
 // rows; each holds half of Q's head dim and half of O. Each computes the
 // partial S^T over its half of the contraction, the pair adds the two halves
 // through LDS (in the same order in both waves, so both hold bit-identical
 // scores and run identical softmax), and each then accumulates its half of O.
-// K and V tiles are still read from LDS exactly once per row block.
 #pragma once
 
 #include "fa_device.h"
@@ -70,30 +76,49 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + k;
 }
 
-// Position inside a 16-key group after exchanging key bits 2 and 3.
-__device__ __forceinline__ int vt_quad_pos(int quad) {
-  return (quad & ~3) | ((quad & 1) << 1) | ((quad >> 1) & 1);
+// XOR swizzles (16-byte chunk index within a row). Both stay below the chunk
+// count of a row.
+//
+// K is read as the A operand of S^T: sixteen consecutive lanes read sixteen
+// consecutive rows at the same logical chunk, so the XOR takes four bits of
+// the row (spreading them over 16 distinct 16-byte bank groups; any 8
+// consecutive lanes also land in 8 distinct groups).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D >= 128) return row & 15;
+  else return (row >> 1) & 7;          // 128-byte rows: two rows per 256 bytes
+}
+// V is read by ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive rows x
+// 2 consecutive chunks, the two groups of a half-wave the next 2 chunks of
+// the same rows. The XOR (bits 1-3) separates the 4 rows both in bits 2-3
+// (16 distinct groups across the half-wave) and in bits 1-2 (8 distinct
+// groups within one 16-lane group).
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  const int rr = row & 3;
+  if constexpr (D >= 128) return (rr << 2) ^ (((rr ^ (rr >> 1)) & 1) << 1);
+  else return rr << 1;
 }
 
-template <int D, int NW, int BN, int DS, bool PAGED, bool SPLIT, bool PREFETCH, int WPE>
+template <int D, int NW, int BN, int DS, bool PAGED, bool SPLIT, int WPE>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert(DS == 1 || (DS == 2 && NW % 2 == 0), "a D split pairs waves");
-  constexpr int T = NW * 64;
   constexpr int BM = NW * 32 / DS;
-  constexpr int KCH = D / 8;                  // 16-byte chunks per K row
-  constexpr int NBUF = PREFETCH ? 2 : 1;
-  constexpr int K_UNITS = BN * KCH;           // one 16-byte chunk each
-  constexpr int K_PER_T = (K_UNITS + T - 1) / T;
-  constexpr int V_UNITS = (BN / 4) * KCH;     // four keys x eight d each
-  constexpr int V_PER_T = (V_UNITS + T - 1) / T;
+  constexpr int KCH = D / 8;                  // 16-byte chunks per row
+  constexpr int NSEG = BN * KCH / 64;         // 1 KiB segments per tile
+  static_assert(NSEG % NW == 0, "every wave loads whole segments");
+  constexpr int SEGW = NSEG / NW;             // segments per wave per operand
   constexpr int NKB = BN / 32;                // 32-key score blocks per tile
   constexpr int NKS = BN / 16;                // 16-key steps of the PV product
   constexpr int NDB = D / 32 / DS;            // 32-wide d blocks of O per wave
   constexpr int NQC = D / 16 / DS;            // 16-wide d steps of Q K^T per wave
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][D * BN];
+  // separate objects per buffer: the loads into one never alias reads of the other
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BN * D];
   // partial scores exchanged by the two waves of a D split, [wave][value][lane]
   __shared__ float sX[DS == 2 ? NW : 1][DS == 2 ? NKB * 16 : 1][64];
 
@@ -179,115 +204,72 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- K/V address function ---------------------------------------------
-  // Element offset of key t's row (KV head g). Callers clamp t into the
-  // sequence, and a block-table entry outside [0, num_pages) is clamped into
-  // range: every load stays inside the cache, so no load needs a guard.
+  // ---- staging: global -> LDS ------------------------------------------
+  // Segment s (1 KiB) of a tile holds chunk positions 64 s .. 64 s + 63 of
+  // the row-major tile: lane L writes position 64 s + L = row * KCH + pc,
+  // holding logical chunk pc ^ swizzle(row) of that key row.
   const int64_t row_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)g * D;
-  auto key_off = [&](int t) -> int64_t {
-    if constexpr (PAGED) {
-      int page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
-      page = min(max(page, 0), a.num_pages - 1);
-      const int64_t slot = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
-      return slot * row_stride + head_off;
-    } else {
-      return ((int64_t)b * a.slots + t) * row_stride + head_off;
-    }
-  };
+  int srow[SEGW];          // key row (inside the tile) of each of this lane's segments
+  uint32_t koff[SEGW];     // element offset of its K chunk inside an unclamped tile
+  uint32_t voff[SEGW];
+#pragma unroll
+  for (int i = 0; i < SEGW; ++i) {
+    const int pos = (wave * SEGW + i) * 64 + lane;
+    const int row = pos / KCH, pc = pos % KCH;
+    srow[i] = row;
+    koff[i] = (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_k<D>(row)));
+    voff[i] = (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_v<D>(row)));
+  }
+  const uint16_t* kseq = a.k + head_off;
+  const uint16_t* vseq = a.v + head_off;
+  if constexpr (!PAGED) {
+    kseq += (int64_t)b * a.slots * row_stride;
+    vseq += (int64_t)b * a.slots * row_stride;
+  }
 
-  // One K unit is a 16-byte chunk of one key row; one V unit is the same
-  // chunk of four consecutive key rows, written to LDS transposed.
   // Keys past the end of the range are clamped onto its last key: their
-  // scores are masked and their V rows get weight exactly 0, so the data
-  // read there never matters (and is always finite in-range data).
-  auto load_k = [&](int tb, int u) -> u32x4 {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (K_UNITS % T == 0 || u < K_UNITS) {
-      const int t = min(tb + u / KCH, ke - 1);
-      w = *reinterpret_cast<const u32x4*>(a.k + key_off(t) + 8 * (u % KCH));
-    }
-    return w;
-  };
-  auto store_k = [&](int buf, int u, const u32x4& w) {
-    if (K_UNITS % T == 0 || u < K_UNITS) {
-      const int key = u / KCH, ch = u % KCH;
-      *reinterpret_cast<u32x4*>(&sK[buf][key * D + 8 * swz_chunk<D * 2>(key, ch)]) = w;
-    }
-  };
-  auto load_v = [&](int tb, int u, u32x4* w4) {
+  // scores are masked and their V rows get weight exactly 0, so the data read
+  // there never matters (and is always finite in-range data). A block-table
+  // entry outside [0, num_pages) is clamped into range: every load stays
+  // inside the cache.
+  auto issue_tile = [&](int tb, uint16_t* dk, uint16_t* dv) {
+    const int lim = ke - 1 - tb;              // last valid row of this tile
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (V_UNITS % T == 0 || u < V_UNITS) {
-        const int t = min(tb + 4 * (u / KCH) + jj, ke - 1);
-        w = *reinterpret_cast<const u32x4*>(a.v + key_off(t) + 8 * (u % KCH));
-      }
-      w4[jj] = w;
-    }
-  };
-  auto store_v = [&](int buf, int u, const u32x4* w4) {
-    if (V_UNITS % T == 0 || u < V_UNITS) {
-      const int dc = u % KCH, quad = u / KCH;
-      const int pos = 4 * vt_quad_pos(quad);     // key position inside the row
-      const int chunk = pos >> 3, half = (pos >> 2) & 1;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        uint32_t x01, x23;
-        if ((dd & 1) == 0) {
-          x01 = pack_lo16(w4[0][w], w4[1][w]);
-          x23 = pack_lo16(w4[2][w], w4[3][w]);
-        } else {
-          x01 = pack_hi16(w4[0][w], w4[1][w]);
-          x23 = pack_hi16(w4[2][w], w4[3][w]);
+    for (int i = 0; i < SEGW; ++i) {
+      const uint16_t* gk;
+      const uint16_t* gv;
+      if constexpr (PAGED) {
+        const int t = tb + min(srow[i], lim);
+        int page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
+        page = min(max(page, 0), a.num_pages - 1);
+        const int64_t base = ((((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1))) -
+                              srow[i]) * row_stride;
+        gk = kseq + base + koff[i];
+        gv = vseq + base + voff[i];
+      } else {
+        const int64_t tile = (int64_t)tb * row_stride;
+        uint32_t ok = koff[i], ov = voff[i];
+        if (srow[i] > lim) {                    // tail tile only
+          const uint32_t back = (uint32_t)((srow[i] - lim) * (int)row_stride);
+          ok -= back;
+          ov -= back;
         }
-        const int d = 8 * dc + dd;
-        u32x2 val = {x01, x23};
-        *reinterpret_cast<u32x2*>(&sV[buf][d * BN + 8 * swz_chunk<BN * 2>(d, chunk) + 4 * half]) = val;
+        gk = kseq + tile + ok;
+        gv = vseq + tile + ov;
       }
+      dma16(gk, dk + (wave * SEGW + i) * 512);
+      dma16(gv, dv + (wave * SEGW + i) * 512);
     }
   };
 
-  // Register double buffer for the prefetching variant.
-  u32x4 kreg[PREFETCH ? K_PER_T : 1];
-  u32x4 vreg[PREFETCH ? V_PER_T : 1][4];
-  auto load_tile = [&](int tb) {
-    if constexpr (PREFETCH) {
-#pragma unroll
-      for (int i = 0; i < K_PER_T; ++i) kreg[i] = load_k(tb, tid + i * T);
-#pragma unroll
-      for (int i = 0; i < V_PER_T; ++i) load_v(tb, tid + i * T, vreg[i]);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if constexpr (PREFETCH) {
-#pragma unroll
-      for (int i = 0; i < K_PER_T; ++i) store_k(buf, tid + i * T, kreg[i]);
-#pragma unroll
-      for (int i = 0; i < V_PER_T; ++i) store_v(buf, tid + i * T, vreg[i]);
-    }
-  };
-  // Direct staging in small pieces (bounded register use).
-  auto stage_tile = [&](int tb, int buf) {
-    constexpr int PK = 4;
-#pragma unroll
-    for (int i0 = 0; i0 < K_PER_T; i0 += PK) {
-      u32x4 w[PK];
-#pragma unroll
-      for (int i = 0; i < PK; ++i)
-        if (i0 + i < K_PER_T) w[i] = load_k(tb, tid + (i0 + i) * T);
-#pragma unroll
-      for (int i = 0; i < PK; ++i)
-        if (i0 + i < K_PER_T) store_k(buf, tid + (i0 + i) * T, w[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      u32x4 w4[4];
-      load_v(tb, tid + i * T, w4);
-      store_v(buf, tid + i * T, w4);
-    }
-  };
+  // ---- LDS read addresses --------------------------------------------------
+  // K (A operand of S^T): row 32 kb + j, logical chunk 2 (c + dh NQC) + hl.
+  // V^T (A operand of O^T): the 16-lane group m = lane % 16 supplies rows
+  // key_base + m / 4 at d = d_base + 4 (m % 4); lane i of the group receives
+  // (V[key_base + e][d_base + i], e = 0..3).
+  const int m16 = lane & 15;
+  const int g1 = (lane >> 4) & 1;
 
   // ---- running state -----------------------------------------------------
   f32x16 oacc[NDB];
@@ -298,7 +280,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   const float sl2 = a.sl2;
   const float thr = kRescaleLog2 / sl2;
 
-  auto compute_tile = [&](int buf, int tb) {
+  auto compute_tile = [&](const uint16_t* bk, const uint16_t* bv, int tb) {
     // wave-uniform: skip tiles with no visible key for any row of the wave
     const bool active = wave_rows && tb < ke && !(a.causal && tb > wpmax) &&
                         !(a.causal && a.window > 0 && tb + BN - 1 <= wpmin - a.window);
@@ -316,8 +298,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < NQC; ++c) {
           const int ch = 2 * (c + dh * NQC) + hl;
-          const u32x4 kw = *reinterpret_cast<const u32x4*>(
-              &sK[buf][row * D + 8 * swz_chunk<D * 2>(row, ch)]);
+          const u32x4 kw = *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
           s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
         }
       }
@@ -394,42 +375,43 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       }
     }
     l_run += ls;
+
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * (db + dh * NDB) + j;
+      const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
+      const int dch = d >> 3, dsub = d & 7;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 vw = *reinterpret_cast<const u32x4*>(
-            &sV[buf][d * BN + 8 * swz_chunk<BN * 2>(d, 2 * ks + hl)]);
+        u32x4 vw;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int row = 16 * ks + 8 * half + 4 * hl + (m16 >> 2);
+          const u32x2 t = read_tr16(&bv[row * D + 8 * (dch ^ swz_v<D>(row)) + dsub]);
+          vw[2 * half] = t[0];
+          vw[2 * half + 1] = t[1];
+        }
         oacc[db] = mfma32(as_bf16x8(vw), as_bf16x8(pf[ks]), oacc[db]);
       }
     }
   };
 
-  // ---- main loop: one barrier per tile -----------------------------------
-  if constexpr (PREFETCH) {
-    if (n_tiles > 0) {
-      load_tile(t_start);
-      store_tile(0);
-    }
+  // ---- main loop: tile t computes while tile t+1 streams in ------------------
+  // One barrier per tile: after it, this tile's loads (issued one tile earlier
+  // and waited for by every wave) are visible, and every wave has finished
+  // the previous tile, so the other buffer can be refilled. The buffer parity
+  // is a compile-time constant in each half of the unrolled pair.
+  if (n_tiles > 0) issue_tile(t_start, sK0, sV0);
+  for (int it = 0; it < n_tiles; it += 2) {
+    const int tb = t_start + it * BN;
+    wait_dma();
     __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-      const int tb = t_start + it * BN;
-      const int cur = it & 1;
-      const bool more = it + 1 < n_tiles;
-      if (more) load_tile(tb + BN);
-      compute_tile(cur, tb);
-      if (more) store_tile(cur ^ 1);
-      __syncthreads();
-    }
-  } else {
-    for (int it = 0; it < n_tiles; ++it) {
-      const int tb = t_start + it * BN;
-      stage_tile(tb, 0);
-      __syncthreads();
-      compute_tile(0, tb);
-      __syncthreads();
-    }
+    if (it + 1 < n_tiles) issue_tile(tb + BN, sK1, sV1);
+    compute_tile(sK0, sV0, tb);
+    if (it + 1 >= n_tiles) break;
+    wait_dma();
+    __syncthreads();
+    if (it + 2 < n_tiles) issue_tile(tb + 2 * BN, sK0, sV0);
+    compute_tile(sK1, sV1, tb + BN);
   }
 
   // ---- epilogue ----------------------------------------------------------

@@ -20,9 +20,7 @@ template <int D, int NWR> struct SplitCfg {
   static constexpr int DS = D >= 256 ? 2 : 1;
   static constexpr int NW = NWR * DS;
   static constexpr int BN = (NWR == 4 && D <= 128) ? 64 : 32;
-  static constexpr bool PF = D <= 256;
-  // one row wave at D = 128 holds a 64-register tile prefetch: one wave per SIMD
-  static constexpr int WPE = (D <= 64 || (D == 128 && NWR > 1)) ? 2 : 1;
+  static constexpr int WPE = D <= 128 ? 2 : 1;
 };
 
 template <int D, int NWR>
@@ -52,10 +50,10 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb * d.max_chunks;
   if (grid == 0) return hipSuccess;
   if (d.table != nullptr)
-    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, true, true, C::PF, C::WPE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, true, true, C::WPE>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, false, true, C::PF, C::WPE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, false, true, C::WPE>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }

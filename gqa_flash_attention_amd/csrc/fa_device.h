@@ -67,18 +67,27 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// 16-byte-chunk XOR swizzle for an LDS tile whose rows are ROW_BYTES long.
-// The 64 four-byte banks repeat every 256 bytes; the XOR spreads sixteen
-// consecutive rows read at the same logical chunk over sixteen distinct
-// 16-byte bank groups. The XOR value stays below the chunk count of a row, so
-// a swizzled chunk never leaves its row.
-template <int ROW_BYTES>
-__device__ __forceinline__ int swz_chunk(int row, int chunk) {
-  constexpr int kRowsPer256 = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
-  constexpr int kSpan = 16 / kRowsPer256;
-  static_assert(ROW_BYTES % 16 == 0 && ROW_BYTES >= 64, "row must hold at least four chunks");
-  static_assert(kSpan <= ROW_BYTES / 16, "swizzle must stay inside the row");
-  return chunk ^ ((row / kRowsPer256) % kSpan);
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4). The LDS
+// destination `lds_seg` must be the same for the whole wave: lane L's 16 bytes
+// land at lds_seg + 16 L bytes.
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_seg) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_seg, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding global loads (including global -> LDS
+// copies) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16). Within
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows
+// addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 (in that
+// order).
+__device__ __forceinline__ u32x2 read_tr16(const uint16_t* lds) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lds);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Element offset of K/V row (sequence b, token t, KV head g) in a cache laid

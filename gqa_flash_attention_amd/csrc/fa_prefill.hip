@@ -7,14 +7,12 @@ namespace gqafa {
 namespace {
 
 // Tile shape per head dim: waves per workgroup, keys per tile, D split (two
-// waves per 32 rows), and whether the next tile is prefetched into registers
-// while the current one computes.
+// waves per 32 rows) and the waves per SIMD the register budget is sized for.
 template <int D> struct PrefillCfg;
-// WPE: waves per SIMD the register budget is sized for.
-template <> struct PrefillCfg<64>  { static constexpr int NW = 4, BN = 64, DS = 1, WPE = 2; static constexpr bool PF = true; };
-template <> struct PrefillCfg<128> { static constexpr int NW = 4, BN = 64, DS = 1, WPE = 2; static constexpr bool PF = true; };
-template <> struct PrefillCfg<256> { static constexpr int NW = 4, BN = 32, DS = 1, WPE = 1; static constexpr bool PF = true; };
-template <> struct PrefillCfg<512> { static constexpr int NW = 4, BN = 32, DS = 2, WPE = 1; static constexpr bool PF = false; };
+template <> struct PrefillCfg<64>  { static constexpr int NW = 4, BN = 64, DS = 1, WPE = 2; };
+template <> struct PrefillCfg<128> { static constexpr int NW = 4, BN = 64, DS = 1, WPE = 2; };
+template <> struct PrefillCfg<256> { static constexpr int NW = 4, BN = 32, DS = 1, WPE = 1; };
+template <> struct PrefillCfg<512> { static constexpr int NW = 4, BN = 32, DS = 2, WPE = 1; };
 
 template <int D>
 hipError_t run(const PrefillDesc& d, hipStream_t stream) {
@@ -35,7 +33,7 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   a.n_rb = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, false, false, C::PF, C::WPE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, false, false, C::WPE>), dim3((unsigned)grid),
                      dim3(C::NW * 64), 0, stream, a);
   return hipGetLastError();
 }
