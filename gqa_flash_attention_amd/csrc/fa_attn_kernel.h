@@ -120,11 +120,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[BN * D];
   // partial scores exchanged by the two waves of a D split, [wave][value][lane]
-  __shared__ float sX[DS == 2 ? NW : 1][DS == 2 ? NKB * 16 : 1][64];
+  __shared__ float sX[DS == 2 ? 2 : 1][DS == 2 ? NW : 1][DS == 2 ? NKB * 16 : 1][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps LDS bases scalar
   const int j = lane & 31;     // this lane's query row inside the wave
   const int hl = lane >> 5;    // lane half
   const int rg = wave / DS;    // row group (32 rows) of this wave
@@ -211,15 +211,15 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   const int64_t row_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)g * D;
   int srow[SEGW];          // key row (inside the tile) of each of this lane's segments
-  uint32_t koff[SEGW];     // element offset of its K chunk inside an unclamped tile
+  uint32_t koff[SEGW];     // byte offset of its K chunk inside an unclamped tile
   uint32_t voff[SEGW];
 #pragma unroll
   for (int i = 0; i < SEGW; ++i) {
     const int pos = (wave * SEGW + i) * 64 + lane;
     const int row = pos / KCH, pc = pos % KCH;
     srow[i] = row;
-    koff[i] = (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_k<D>(row)));
-    voff[i] = (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_v<D>(row)));
+    koff[i] = 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_k<D>(row)));
+    voff[i] = 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_v<D>(row)));
   }
   const uint16_t* kseq = a.k + head_off;
   const uint16_t* vseq = a.v + head_off;
@@ -233,35 +233,30 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // there never matters (and is always finite in-range data). A block-table
   // entry outside [0, num_pages) is clamped into range: every load stays
   // inside the cache.
-  auto issue_tile = [&](int tb, uint16_t* dk, uint16_t* dv) {
+  auto issue = [&](int tb, const uint16_t* seq, const uint32_t (&off)[SEGW], uint16_t* dst) {
     const int lim = ke - 1 - tb;              // last valid row of this tile
+    const bool tail = lim < BN - 1;           // uniform
 #pragma unroll
     for (int i = 0; i < SEGW; ++i) {
-      const uint16_t* gk;
-      const uint16_t* gv;
+      const char* src;
       if constexpr (PAGED) {
         const int t = tb + min(srow[i], lim);
         int page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
         page = min(max(page, 0), a.num_pages - 1);
         const int64_t base = ((((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1))) -
                               srow[i]) * row_stride;
-        gk = kseq + base + koff[i];
-        gv = vseq + base + voff[i];
+        src = reinterpret_cast<const char*>(seq + base) + off[i];
       } else {
-        const int64_t tile = (int64_t)tb * row_stride;
-        uint32_t ok = koff[i], ov = voff[i];
-        if (srow[i] > lim) {                    // tail tile only
-          const uint32_t back = (uint32_t)((srow[i] - lim) * (int)row_stride);
-          ok -= back;
-          ov -= back;
-        }
-        gk = kseq + tile + ok;
-        gv = vseq + tile + ov;
+        // uniform tile base + 32-bit per-lane byte offset
+        uint32_t o = off[i];
+        if (tail && srow[i] > lim) o -= 2u * (uint32_t)((srow[i] - lim) * (int)row_stride);
+        src = reinterpret_cast<const char*>(seq + (int64_t)tb * row_stride) + o;
       }
-      dma16(gk, dk + (wave * SEGW + i) * 512);
-      dma16(gv, dv + (wave * SEGW + i) * 512);
+      dma16(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
     }
   };
+  auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, kseq, koff, dst); };
+  auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, vseq, voff, dst); };
 
   // ---- LDS read addresses --------------------------------------------------
   // K (A operand of S^T): row 32 kb + j, logical chunk 2 (c + dh NQC) + hl.
@@ -280,48 +275,27 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   const float sl2 = a.sl2;
   const float thr = kRescaleLog2 / sl2;
 
-  auto compute_tile = [&](const uint16_t* bk, const uint16_t* bv, int tb) {
-    // wave-uniform: skip tiles with no visible key for any row of the wave
-    const bool active = wave_rows && tb < ke && !(a.causal && tb > wpmax) &&
-                        !(a.causal && a.window > 0 && tb + BN - 1 <= wpmin - a.window);
-    if (DS == 1 && !active) return;
-    const bool full = (tb + BN <= ke) && (!a.causal || tb + BN - 1 <= wpmin) &&
-                      (!a.causal || a.window <= 0 || wpmax - tb < a.window);
-
-    f32x16 s[NKB];
+  // S^T (this wave's part of the contraction) for the tile in bk
+  auto scores = [&](const uint16_t* bk, f32x16 (&s)[NKB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-    if (active) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int c = 0; c < NQC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {          // alternate accumulators
         const int row = 32 * kb + j;
-#pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-          const int ch = 2 * (c + dh * NQC) + hl;
-          const u32x4 kw = *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
-          s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
-        }
+        const int ch = 2 * (c + dh * NQC) + hl;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
+        s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
       }
     }
-    if constexpr (DS == 2) {
-      if (active) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) sX[wave][kb * 16 + x][lane] = s[kb][x];
-      }
-      __syncthreads();
-      if (!active) return;
-      // lower half first in both waves: identical sums in the pair
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float other = sX[wave ^ 1][kb * 16 + x][lane];
-          s[kb][x] = dh == 0 ? s[kb][x] + other : other + s[kb][x];
-        }
-    }
+  };
 
+  // Mask the boundary tiles, update the reference max (lazily), and return
+  // the exponent offset -m*c for the tile starting at key tb.
+  auto prepare = [&](f32x16 (&s)[NKB], int tb) -> float {
+    const bool full = (tb + BN <= ke) && (!a.causal || tb + BN - 1 <= wpmin) &&
+                      (!a.causal || a.window <= 0 || wpmax - tb < a.window);
     if (!full) {
       // visible iff lo_lim <= key - tb - 4*hl <= hi_lim; the left side is a
       // per-element constant
@@ -336,7 +310,6 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           s[kb][x] = (rel <= hi_lim && rel >= lo_lim) ? s[kb][x] : -INFINITY;
         }
     }
-
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -356,12 +329,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
-    const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
+    return m_run == -INFINITY ? 0.f : -m_run * sl2;
+  };
 
-    // P = exp2(s*c - m*c) as bf16 pairs: already the B operand of O^T += V^T P^T.
-    // The row sum adds the fp32 values: with few visible keys, summing the
-    // bf16-rounded P would put bf16's 2^-9 relative error straight into LSE.
-    u32x4 pf[NKS];
+  // P = exp2(s*c - m*c) as bf16 pairs: already the B operand of O^T += V^T P^T.
+  // The row sum adds the fp32 values: with few visible keys, summing the
+  // bf16-rounded P would put bf16's 2^-9 relative error straight into LSE.
+  auto exponentiate = [&](const f32x16 (&s)[NKB], float nb, u32x4 (&pf)[NKS]) {
     float ls = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -375,13 +349,17 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       }
     }
     l_run += ls;
+  };
 
+  // O^T += V^T P^T for the tile in bv
+  auto accumulate = [&](const uint16_t* bv, const u32x4 (&pf)[NKS]) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
-      const int dch = d >> 3, dsub = d & 7;
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int db = 0; db < NDB; ++db) {
+        // consecutive MFMAs feed different accumulators
+        const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
+        const int dch = d >> 3, dsub = d & 7;
         u32x4 vw;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -395,23 +373,75 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
   };
 
-  // ---- main loop: tile t computes while tile t+1 streams in ------------------
-  // One barrier per tile: after it, this tile's loads (issued one tile earlier
-  // and waited for by every wave) are visible, and every wave has finished
-  // the previous tile, so the other buffer can be refilled. The buffer parity
-  // is a compile-time constant in each half of the unrolled pair.
-  if (n_tiles > 0) issue_tile(t_start, sK0, sV0);
-  for (int it = 0; it < n_tiles; it += 2) {
+  // D split: publish this wave's partial scores, and add the partner's.
+  auto publish = [&](const f32x16 (&s)[NKB], int slot) {
+    if constexpr (DS == 2) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) sX[slot][wave][kb * 16 + x][lane] = s[kb][x];
+    }
+  };
+  auto combine_partner = [&](f32x16 (&s)[NKB], int slot) {
+    if constexpr (DS == 2) {
+      // lower half first in both waves: identical sums in the pair
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const float other = sX[slot][wave ^ 1][kb * 16 + x][lane];
+          s[kb][x] = dh == 0 ? s[kb][x] + other : other + s[kb][x];
+        }
+    }
+  };
+
+  // VALU instructions of one tile's exponentiation per lane: an FMA and an
+  // exp per score, one add per score and one pack per pair
+  constexpr int kExpValuPerTile = NKB * 16 * 3 + NKB * 8;
+
+  // ---- main loop, software-pipelined -----------------------------------------
+  // Step t: the scores of tile t are already in registers. After the barrier
+  // (tile t+1's K and tile t's V have landed in LDS, and every wave is done
+  // with step t-1), the wave starts the copies of K(t+2) and V(t+1) into the
+  // buffers step t-1 released, runs the S^T MFMAs of tile t+1 while the VALU
+  // exponentiates tile t, then accumulates O with tile t's V. The MFMA work
+  // of S(t+1) thus overlaps the softmax of tile t inside one wave. The buffer
+  // parity is a compile-time constant in each half of the unrolled pair.
+  f32x16 sc[NKB];
+  if (n_tiles > 0) {
+    issue_k(t_start, sK0);
+    issue_v(t_start, sV0);
+    wait_dma();
+    __syncthreads();
+    if (n_tiles > 1) issue_k(t_start + BN, sK1);
+    scores(sK0, sc);
+    publish(sc, 0);
+  }
+  auto step = [&](int it, uint16_t* k_cur, uint16_t* k_next, uint16_t* v_cur, uint16_t* v_next) {
     const int tb = t_start + it * BN;
     wait_dma();
     __syncthreads();
-    if (it + 1 < n_tiles) issue_tile(tb + BN, sK1, sV1);
-    compute_tile(sK0, sV0, tb);
+    if (it + 2 < n_tiles) issue_k(tb + 2 * BN, k_cur);
+    if (it + 1 < n_tiles) issue_v(tb + BN, v_next);
+    combine_partner(sc, it & 1);
+    const float nb = prepare(sc, tb);
+    f32x16 sn[NKB];
+    scores(k_next, sn);               // tile t+1 (unused after the last tile)
+    u32x4 pf[NKS];
+    exponentiate(sc, nb, pf);
+    publish(sn, (it + 1) & 1);
+    accumulate(v_cur, pf);
+    // one schedule for the whole step: S(t+1) MFMAs each followed by the
+    // next K read and a share of tile t's exponentiation, then the PV MFMAs
+    // each followed by the next two V^T reads
+    sched_step<NKB * NQC, 1, NDB * NKS, 2, 4, kExpValuPerTile / (NKB * NQC)>();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(it, sK0, sK1, sV0, sV1);
     if (it + 1 >= n_tiles) break;
-    wait_dma();
-    __syncthreads();
-    if (it + 2 < n_tiles) issue_tile(tb + 2 * BN, sK0, sV0);
-    compute_tile(sK1, sV1, tb + BN);
+    step(it + 1, sK1, sK0, sV1, sV0);
   }
 
   // ---- epilogue ----------------------------------------------------------

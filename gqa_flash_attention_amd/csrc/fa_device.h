@@ -75,6 +75,32 @@ __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_seg) {
                                    (__attribute__((address_space(3))) void*)lds_seg, 16, 0, 0);
 }
 
+// Scheduling hints (sched_group_barrier masks: 0x2 VALU, 0x8 MFMA, 0x100
+// DS read). One pipeline step: N1 MFMAs that each consume R1 LDS reads and
+// may hide V1 VALU instructions, then N2 MFMAs consuming R2 reads each. The
+// reads run AHEAD reads in front of their MFMAs.
+template <int N, int R, int AHEAD, int V, int I>
+__device__ __forceinline__ void sched_phase() {
+  if constexpr (I < N) {
+    constexpr int total = N * R;
+    constexpr int lo = I * R + AHEAD < total ? I * R + AHEAD : total;
+    constexpr int hi = (I + 1) * R + AHEAD < total ? (I + 1) * R + AHEAD : total;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    sched_phase<N, R, AHEAD, V, I + 1>();
+  }
+}
+template <int N1, int R1, int N2, int R2, int AHEAD, int V1>
+__device__ __forceinline__ void sched_step() {
+  constexpr int a1 = AHEAD < N1 * R1 ? AHEAD : N1 * R1;
+  __builtin_amdgcn_sched_group_barrier(0x100, a1, 0);
+  sched_phase<N1, R1, a1, V1, 0>();
+  constexpr int a2 = AHEAD < N2 * R2 ? AHEAD : N2 * R2;
+  __builtin_amdgcn_sched_group_barrier(0x100, a2, 0);
+  sched_phase<N2, R2, a2, 0, 0>();
+}
+
 // Wait until this wave's outstanding global loads (including global -> LDS
 // copies) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
