@@ -105,6 +105,7 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   if ((int64_t)B * Hkv * ((rows + 31) / 32) * (max_chunks > 0 ? max_chunks : 1) > kMaxGrid)
     return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;   // one combine workgroup per row
 
   const int64_t prow = (int64_t)B * Hq * Sq;
   float* o_part = static_cast<float*>(workspace);
@@ -131,7 +132,7 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
   if (!o || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (max_chunks > 0 && (!o_part || !lse_part || !aligned16(o_part))) return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
-  if (((int64_t)B * Hq * Sq + 3) / 4 > kMaxGrid) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
   CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, B, Sq, Hq, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
 }

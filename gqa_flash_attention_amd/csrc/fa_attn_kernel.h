@@ -63,7 +63,8 @@ struct AttnArgs {
   int causal, window;
   float sl2;              // scale * log2(e)
   int n_rb;               // row blocks per (b, g)
-  int chunk, max_chunks;  // split mode
+  int chunk, max_chunks;  // split mode: keys per partial, partial slots per row
+  int cpw, n_cg;          // split mode: chunks per workgroup, chunk groups per row block
 };
 
 // Spread a 1-D grid over the 8 XCDs so that logical neighbours (row blocks of
@@ -100,10 +101,10 @@ __device__ __forceinline__ int swz_v(int row) {
   else return rr << 1;
 }
 
-template <int D, int NW, int BN, int DS, bool PAGED, bool SPLIT, int WPE>
+template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, bool MULTI, int WPE>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(DS == 1 || (DS == 2 && NW % 2 == 0), "a D split pairs waves");
+  static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
   constexpr int BM = NW * 32 / DS;
   constexpr int KCH = D / 8;                  // 16-byte chunks per row
   constexpr int NSEG = BN * KCH / 64;         // 1 KiB segments per tile
@@ -113,14 +114,31 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   constexpr int NKS = BN / 16;                // 16-key steps of the PV product
   constexpr int NDB = D / 32 / DS;            // 32-wide d blocks of O per wave
   constexpr int NQC = D / 16 / DS;            // 16-wide d steps of Q K^T per wave
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tile buffers per operand");
+  static_assert(SPLIT || !MULTI, "several chunks per workgroup only in split mode");
+  // block-table entries staged in LDS (none at D = 512, where the tile ring
+  // and the score exchange fill LDS)
+  constexpr int TAB = (PAGED && SPLIT && D < 512) ? 2048 : 0;
 
-  // separate objects per buffer: the loads into one never alias reads of the other
+  // A ring of NBUF tile buffers per operand, each its own object: the copies
+  // into one never alias reads of another, so no read waits on a copy it does
+  // not need.
+  constexpr int B2 = NBUF > 2 ? BN * D : 8, B3 = NBUF > 3 ? BN * D : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK2[B2];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK3[B3];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[BN * D];
-  // partial scores exchanged by the two waves of a D split, [wave][value][lane]
-  __shared__ float sX[DS == 2 ? 2 : 1][DS == 2 ? NW : 1][DS == 2 ? NKB * 16 : 1][64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV2[B2];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV3[B3];
+  int* sT = nullptr;
+  if constexpr (TAB > 0) {
+    __shared__ int sT_buf[TAB > 0 ? TAB : 1];
+    sT = sT_buf;
+  }
+  // partial scores exchanged by the waves of a D split, [slot][wave][value][lane]
+  __shared__ float sX[DS > 1 ? 2 : 1][DS > 1 ? NW : 1][DS > 1 ? NKB * 16 : 1][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -131,15 +149,18 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   const int dh = wave % DS;    // which half of the head dim this wave holds
 
   // ---- work item -------------------------------------------------------
-  int b, g, rb, cid = 0;
+  int b, g, rb, cg = 0;
   if constexpr (SPLIT) {
+    // KV head fastest: the workgroups reading the Hkv head slices of one
+    // token range run side by side, so together they read whole token rows
+    // ([.., Hkv, D] is token-major) instead of scattered head slices
     int L = blockIdx.x;
-    cid = L % a.max_chunks;
-    L /= a.max_chunks;
+    g = L % a.Hkv;
+    L /= a.Hkv;
     rb = L % a.n_rb;
-    const int bg = L / a.n_rb;
-    b = bg / a.Hkv;
-    g = bg % a.Hkv;
+    L /= a.n_rb;
+    cg = L % a.n_cg;
+    b = L / a.n_cg;
   } else {
     const int n = a.B * a.Hkv * a.n_rb;
     const int L = xcd_remap(blockIdx.x, n);
@@ -150,12 +171,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   }
 
   int n_keys;
+  int c0 = 0, c1 = 1;   // split mode: this workgroup's partials [c0, c1)
   if constexpr (SPLIT) {
     const int64_t cap = (int64_t)a.max_pages << a.page_shift;
     int64_t sl = a.seq_lens[b];
     sl = sl < 0 ? 0 : (sl > cap ? cap : sl);
     n_keys = (int)sl;
-    if ((int64_t)cid * a.chunk >= n_keys) return;  // past the end: the merge skips it
+    const int nch = (int)((sl + a.chunk - 1) / a.chunk);
+    c0 = cg * a.cpw;
+    if (c0 >= nch) return;  // past the end: the merge reads no partial here
+    c1 = min(c0 + a.cpw, nch);
   } else {
     n_keys = a.skv;
   }
@@ -170,8 +195,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // keys this workgroup may need: [kv_lo, kv_hi), inside the split [kb0, ke)
   int kb0 = 0, ke = n_keys;
   if constexpr (SPLIT) {
-    kb0 = cid * a.chunk;
-    ke = min(n_keys, kb0 + a.chunk);
+    kb0 = c0 * a.chunk;
+    ke = (int)min((int64_t)n_keys, (int64_t)c1 * a.chunk);
   }
   int kv_lo = kb0, kv_hi = ke;
   if (a.causal) {
@@ -210,16 +235,31 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // holding logical chunk pc ^ swizzle(row) of that key row.
   const int64_t row_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)g * D;
-  int srow[SEGW];          // key row (inside the tile) of each of this lane's segments
-  uint32_t koff[SEGW];     // byte offset of its K chunk inside an unclamped tile
-  uint32_t voff[SEGW];
+  // Per-lane segment geometry. With few segments per wave it is kept in
+  // registers; with many (large head dims, few waves) it is recomputed at
+  // each copy, which costs a few integer operations instead of 3 registers
+  // per segment.
+  constexpr bool KEEP_SEG = SEGW <= 8;
+  constexpr int NKEEP = KEEP_SEG ? SEGW : 1;
+  auto seg_row = [&](int i) -> int { return ((wave * SEGW + i) * 64 + lane) / KCH; };
+  auto seg_koff = [&](int i) -> uint32_t {
+    const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
+    return 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_k<D>(row)));
+  };
+  auto seg_voff = [&](int i) -> uint32_t {
+    const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
+    return 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_v<D>(row)));
+  };
+  int srow[NKEEP];         // key row (inside the tile) of each of this lane's segments
+  uint32_t koff[NKEEP];    // byte offset of its K chunk inside an unclamped tile
+  uint32_t voff[NKEEP];
+  if constexpr (KEEP_SEG) {
 #pragma unroll
-  for (int i = 0; i < SEGW; ++i) {
-    const int pos = (wave * SEGW + i) * 64 + lane;
-    const int row = pos / KCH, pc = pos % KCH;
-    srow[i] = row;
-    koff[i] = 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_k<D>(row)));
-    voff[i] = 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_v<D>(row)));
+    for (int i = 0; i < SEGW; ++i) {
+      srow[i] = seg_row(i);
+      koff[i] = seg_koff(i);
+      voff[i] = seg_voff(i);
+    }
   }
   const uint16_t* kseq = a.k + head_off;
   const uint16_t* vseq = a.v + head_off;
@@ -228,35 +268,61 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     vseq += (int64_t)b * a.slots * row_stride;
   }
 
+  // Paged split: the workgroup's slice of the block table (clamped into
+  // [0, num_pages)) is staged in LDS once, so no tile copy waits on a table
+  // load; a slice longer than the staging area is read from global memory.
+  int p0 = 0;
+  bool tab_lds = false;
+  if constexpr (PAGED && SPLIT) {
+    p0 = kb0 >> a.page_shift;
+    const int np = ke > kb0 ? ((ke - 1) >> a.page_shift) - p0 + 1 : 0;
+    tab_lds = TAB > 0 && np <= TAB;
+    if (tab_lds) {
+      for (int i = tid; i < np; i += NW * 64) {
+        const int page = a.table[(int64_t)b * a.max_pages + p0 + i];
+        sT[i] = min(max(page, 0), a.num_pages - 1);
+      }
+    }
+    __syncthreads();
+  }
+
   // Keys past the end of the range are clamped onto its last key: their
   // scores are masked and their V rows get weight exactly 0, so the data read
   // there never matters (and is always finite in-range data). A block-table
   // entry outside [0, num_pages) is clamped into range: every load stays
   // inside the cache.
-  auto issue = [&](int tb, const uint16_t* seq, const uint32_t (&off)[SEGW], uint16_t* dst) {
+  auto issue = [&](int tb, bool is_v, uint16_t* dst) {
+    const uint16_t* seq = is_v ? vseq : kseq;
     const int lim = ke - 1 - tb;              // last valid row of this tile
     const bool tail = lim < BN - 1;           // uniform
 #pragma unroll
     for (int i = 0; i < SEGW; ++i) {
+      const int row = KEEP_SEG ? srow[i] : seg_row(i);
+      const uint32_t off0 = KEEP_SEG ? (is_v ? voff[i] : koff[i]) : (is_v ? seg_voff(i) : seg_koff(i));
       const char* src;
       if constexpr (PAGED) {
-        const int t = tb + min(srow[i], lim);
-        int page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
-        page = min(max(page, 0), a.num_pages - 1);
+        const int t = tb + min(row, lim);
+        int page;
+        if (tab_lds) {
+          page = sT[(t >> a.page_shift) - p0];
+        } else {
+          page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
+          page = min(max(page, 0), a.num_pages - 1);
+        }
         const int64_t base = ((((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1))) -
-                              srow[i]) * row_stride;
-        src = reinterpret_cast<const char*>(seq + base) + off[i];
+                              row) * row_stride;
+        src = reinterpret_cast<const char*>(seq + base) + off0;
       } else {
         // uniform tile base + 32-bit per-lane byte offset
-        uint32_t o = off[i];
-        if (tail && srow[i] > lim) o -= 2u * (uint32_t)((srow[i] - lim) * (int)row_stride);
+        uint32_t o = off0;
+        if (tail && row > lim) o -= 2u * (uint32_t)((row - lim) * (int)row_stride);
         src = reinterpret_cast<const char*>(seq + (int64_t)tb * row_stride) + o;
       }
-      dma16(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
+      dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
     }
   };
-  auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, kseq, koff, dst); };
-  auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, vseq, voff, dst); };
+  auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, false, dst); };
+  auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, true, dst); };
 
   // ---- LDS read addresses --------------------------------------------------
   // K (A operand of S^T): row 32 kb + j, logical chunk 2 (c + dh NQC) + hl.
@@ -373,9 +439,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
   };
 
-  // D split: publish this wave's partial scores, and add the partner's.
+  // D split: publish this wave's partial scores, and add the group's.
   auto publish = [&](const f32x16 (&s)[NKB], int slot) {
-    if constexpr (DS == 2) {
+    if constexpr (DS > 1) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -383,14 +449,30 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
   };
   auto combine_partner = [&](f32x16 (&s)[NKB], int slot) {
-    if constexpr (DS == 2) {
-      // lower half first in both waves: identical sums in the pair
+    if constexpr (DS > 1) {
+      // every wave of the group adds the DS parts in the same order (part 0
+      // first), so all of them hold bit-identical scores; only the other
+      // waves' parts are read back
+      const int w0 = rg * DS;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const float other = sX[slot][wave ^ 1][kb * 16 + x][lane];
-          s[kb][x] = dh == 0 ? s[kb][x] + other : other + s[kb][x];
+          if constexpr (DS == 2) {
+            const float other = sX[slot][wave ^ 1][kb * 16 + x][lane];
+            s[kb][x] = dh == 0 ? s[kb][x] + other : other + s[kb][x];
+          } else {
+            float part[DS];
+#pragma unroll
+            for (int k = 0; k < DS; ++k) part[k] = s[kb][x];
+#pragma unroll
+            for (int k = 0; k < DS; ++k)
+              if (k != dh) part[k] = sX[slot][w0 + k][kb * 16 + x][lane];
+            float acc = part[0];
+#pragma unroll
+            for (int k = 1; k < DS; ++k) acc += part[k];
+            s[kb][x] = acc;
+          }
         }
     }
   };
@@ -402,69 +484,115 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // ---- main loop, software-pipelined -----------------------------------------
   // Step t: the scores of tile t are already in registers. After the barrier
   // (tile t+1's K and tile t's V have landed in LDS, and every wave is done
-  // with step t-1), the wave starts the copies of K(t+2) and V(t+1) into the
-  // buffers step t-1 released, runs the S^T MFMAs of tile t+1 while the VALU
-  // exponentiates tile t, then accumulates O with tile t's V. The MFMA work
-  // of S(t+1) thus overlaps the softmax of tile t inside one wave. The buffer
-  // parity is a compile-time constant in each half of the unrolled pair.
+  // with step t-1), the wave starts the copies of K(t+NBUF) and V(t+NBUF-1)
+  // into the buffers step t-1 released, runs the S^T MFMAs of tile t+1 while
+  // the VALU exponentiates tile t, then accumulates O with tile t's V. The
+  // MFMA work of S(t+1) overlaps the softmax of tile t inside one wave, and
+  // NBUF-1 tiles of copies stay in flight. The copies of one step (K(t+1+j),
+  // V(t+j)) form a group; the wait before step t lets the groups issued after
+  // group t stay outstanding. Buffer indices are compile-time constants in
+  // the unrolled ring.
+  auto kbuf = [&](int i) -> uint16_t* { return i == 0 ? sK0 : i == 1 ? sK1 : i == 2 ? sK2 : sK3; };
+  auto vbuf = [&](int i) -> uint16_t* { return i == 0 ? sV0 : i == 1 ? sV1 : i == 2 ? sV2 : sV3; };
+  constexpr int GROUP = 2 * SEGW;                         // copy instructions per group
+  constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
+  constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
+
+  // split mode: finish the partial of chunk c with the current state, then
+  // start the next chunk from scratch
+  int cur_chunk = SPLIT ? t_start / a.chunk : 0;
+  auto write_partial = [&](int c) {
+    const float l_tot = pair_sum(l_run);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : fast_rcp(l_tot);
+    const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
+    if (row_ok) {
+      const int64_t prow = (((int64_t)b * a.Hq + qh) * a.Sq + qi) * a.max_chunks + c;
+      float* dst = a.o_part + prow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
+          f32x4 val = {oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv,
+                       oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv};
+          *reinterpret_cast<f32x4*>(dst + d0) = val;
+        }
+      if (hl == 0 && dh == 0) a.lse_part[prow] = lse_v;
+    }
+  };
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+
   f32x16 sc[NKB];
   if (n_tiles > 0) {
-    issue_k(t_start, sK0);
-    issue_v(t_start, sV0);
-    wait_dma();
+    issue_k(t_start, kbuf(0));
+#pragma unroll
+    for (int jj = 0; jj < NBUF - 1; ++jj) {
+      if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
+      if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
+    }
+    if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
     __syncthreads();
-    if (n_tiles > 1) issue_k(t_start + BN, sK1);
-    scores(sK0, sc);
+    scores(kbuf(0), sc);
     publish(sc, 0);
   }
-  auto step = [&](int it, uint16_t* k_cur, uint16_t* k_next, uint16_t* v_cur, uint16_t* v_next) {
+  auto step = [&](int it, int u) {
     const int tb = t_start + it * BN;
-    wait_dma();
+    if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
     __syncthreads();
-    if (it + 2 < n_tiles) issue_k(tb + 2 * BN, k_cur);
-    if (it + 1 < n_tiles) issue_v(tb + BN, v_next);
+    if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
+    if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
+    if constexpr (SPLIT && MULTI) {
+      if (tb / a.chunk != cur_chunk) {      // uniform: first tile of the next chunk
+        write_partial(cur_chunk);
+        reset_state();
+        cur_chunk = tb / a.chunk;
+      }
+    }
     combine_partner(sc, it & 1);
     const float nb = prepare(sc, tb);
     f32x16 sn[NKB];
-    scores(k_next, sn);               // tile t+1 (unused after the last tile)
+    scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
     u32x4 pf[NKS];
     exponentiate(sc, nb, pf);
     publish(sn, (it + 1) & 1);
-    accumulate(v_cur, pf);
+    accumulate(vbuf(u), pf);
     // one schedule for the whole step: S(t+1) MFMAs each followed by the
     // next K read and a share of tile t's exponentiation, then the PV MFMAs
     // each followed by the next two V^T reads
-    sched_step<NKB * NQC, 1, NDB * NKS, 2, 4, kExpValuPerTile / (NKB * NQC)>();
+    sched_step<NKB * NQC, 1, NDB * NKS, 2, (D >= 512 ? 2 : 4), kExpValuPerTile / (NKB * NQC)>();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
   };
-  for (int it = 0; it < n_tiles; it += 2) {
-    step(it, sK0, sK1, sV0, sV1);
-    if (it + 1 >= n_tiles) break;
-    step(it + 1, sK1, sK0, sV1, sV0);
+  for (int it = 0; it < n_tiles; it += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (it + u >= n_tiles) break;
+      step(it + u, u);
+    }
   }
 
   // ---- epilogue ----------------------------------------------------------
-  const float l_tot = pair_sum(l_run);
-  if (!row_ok) return;
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : fast_rcp(l_tot);
-  const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
-
   if constexpr (SPLIT) {
-    const int64_t prow = (((int64_t)b * a.Hq + qh) * a.Sq + qi) * a.max_chunks + cid;
-    float* dst = a.o_part + prow * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
-        f32x4 val = {oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv,
-                     oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv};
-        *reinterpret_cast<f32x4*>(dst + d0) = val;
-      }
-    if (hl == 0 && dh == 0) a.lse_part[prow] = lse_v;
+    // the chunk of the last tile holds the running state; every other
+    // partial of [c0, c1) that no tile reached (wholly masked) is empty
+    const int c_last = n_tiles > 0 ? (t_start + (n_tiles - 1) * BN) / a.chunk : -1;
+    const int c_first = n_tiles > 0 ? t_start / a.chunk : 0;
+    if (n_tiles > 0) write_partial(c_last);
+    reset_state();
+    for (int c = c0; c < c1; ++c)
+      if (n_tiles == 0 || c < c_first || c > c_last) write_partial(c);
   } else {
+    const float l_tot = pair_sum(l_run);
+    if (!row_ok) return;
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : fast_rcp(l_tot);
+    const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
     uint16_t* dst = a.o + (((int64_t)b * a.Sq + qi) * a.Hq + qh) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

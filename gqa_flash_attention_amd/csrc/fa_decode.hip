@@ -7,6 +7,8 @@
 // by their LSE (beellama.cpp PR 149: a combine kernel runs after the split
 // blocks when the KV range is split into parallel blocks, on the same stream,
 // and every partial must publish its (max, rowsum)).
+#include <algorithm>
+
 #include "fa_attn_kernel.h"
 #include "fa_launch.h"
 
@@ -14,13 +16,18 @@ namespace gqafa {
 
 namespace {
 
-// Split-kernel tile shape by head dim and row waves (32 rows each). Head dims
-// of 256 and above pair two waves per 32 rows (D split).
+// Split-kernel tile shape by head dim and row waves (32 rows each). Head dim
+// 256 splits D over two waves per 32 rows, head dim 512 over four.
 template <int D, int NWR> struct SplitCfg {
-  static constexpr int DS = D >= 256 ? 2 : 1;
+  static constexpr int DS = D >= 512 ? 4 : (D >= 256 ? 2 : 1);
   static constexpr int NW = NWR * DS;
   static constexpr int BN = (NWR == 4 && D <= 128) ? 64 : 32;
   static constexpr int WPE = D <= 128 ? 2 : 1;
+  // tile buffers per operand (measured on MI355X: one row wave streams best
+  // with two, a two-wave block with three; larger head dims are LDS-bound)
+  static constexpr int NBUF = D == 512 ? 2 : (D == 256 ? 3 : ((NWR == 1 || BN * D >= 8192) ? 2 : 3));
+  // several chunks per workgroup
+  static constexpr bool MULTI = true;
 };
 
 template <int D, int NWR>
@@ -47,13 +54,23 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   a.n_rb = (int)((rows + BM - 1) / BM);
   a.chunk = d.kv_chunk;
   a.max_chunks = d.max_chunks;
-  const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb * d.max_chunks;
+  // Very large grids of short chunks merge several consecutive chunks into
+  // one workgroup, whose copy stream then runs across chunk boundaries (one
+  // partial per chunk is still written); chunks must be whole tiles for this.
+  // Up to 16384 chunk slots, one chunk per workgroup streams best.
+  const int64_t slots = (int64_t)d.B * d.Hkv * a.n_rb * d.max_chunks;
+  int cpw = 1;
+  if (C::MULTI && d.kv_chunk % C::BN == 0 && slots > 16384)
+    cpw = (int)std::min<int64_t>(d.max_chunks, (slots + 16383) / 16384);
+  a.cpw = cpw;
+  a.n_cg = (d.max_chunks + cpw - 1) / cpw;
+  const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb * a.n_cg;
   if (grid == 0) return hipSuccess;
   if (d.table != nullptr)
-    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, true, true, C::WPE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::MULTI, C::WPE>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, false, true, C::WPE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::MULTI, C::WPE>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
@@ -61,10 +78,13 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
 template <int D>
 hipError_t run_split_d(const SplitDesc& d, hipStream_t stream) {
   const int64_t rows = (int64_t)d.Sq * (d.Hq / d.Hkv);
-  if (rows <= 32) return run_split<D, 1>(d, stream);
-  if constexpr (D >= 256) {
+  if constexpr (D >= 512) {
+    return run_split<D, 1>(d, stream);      // LDS holds one 32-row block at D = 512
+  } else if constexpr (D >= 256) {
+    if (rows <= 32) return run_split<D, 1>(d, stream);
     return run_split<D, 2>(d, stream);
   } else {
+    if (rows <= 32) return run_split<D, 1>(d, stream);
     if (rows <= 64) return run_split<D, 2>(d, stream);
     return run_split<D, 4>(d, stream);
   }
@@ -92,14 +112,22 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per output row (sequence b, query head h, query row i).
+// One wave (one workgroup) per output row (sequence b, query head h, query
+// row i), in two memory round trips: every LSE of the row at once (lane k
+// holds chunks k and k + 64, ...), then every partial slice the lane needs.
+// The lanes cover (chunk, 16-byte slice of D) pairs: with D/4 slices per
+// chunk, CPI = 64 / (D/4) chunks per step (D <= 256), or SPL = (D/4) / 64
+// slices of one chunk per lane (D = 512). A chunk's weight comes from the
+// lane holding its LSE by a lane shuffle.
 template <int D>
-__global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c) {
-  constexpr int VPL = D / 64;   // output values per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t total = (int64_t)c.B * c.Hq * c.Sq;
-  if (row >= total) return;
+__global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
+  constexpr int SL = D / 4;                       // float4 slices per chunk
+  constexpr int CPI = SL >= 64 ? 1 : 64 / SL;     // chunks per step
+  constexpr int SPL = SL >= 64 ? SL / 64 : 1;     // slices per lane
+  constexpr int MAXL = 4;                          // LSEs held per lane: up to 256 chunks at once
+  constexpr int BATCH = 8;                         // partial loads in flight per lane
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
   const int i = (int)(row % c.Sq);
   const int64_t t = row / c.Sq;
   const int h = (int)(t % c.Hq);
@@ -115,36 +143,75 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c) {
   n = max(0, min(n, c.max_chunks));
 
   const float* lp = c.lse_part + row * c.max_chunks;
+  float lv[MAXL];
   float m = -INFINITY;
-  for (int k = lane; k < n; k += 64) m = fmaxf(m, lp[k]);
+#pragma unroll
+  for (int r = 0; r < MAXL; ++r) {
+    const int k = lane + 64 * r;
+    lv[r] = k < n ? lp[k] : -INFINITY;
+    m = fmaxf(m, lv[r]);
+  }
+  for (int k = lane + 64 * MAXL; k < n; k += 64) m = fmaxf(m, lp[k]);   // rows with > 256 chunks
   m = wave_max(m);
 
-  uint16_t* dst = c.o + (((int64_t)b * c.Sq + i) * c.Hq + h) * D + lane * VPL;
-  float acc[VPL];
+  const int co = CPI > 1 ? lane / SL : 0;         // chunk offset of this lane in a step
+  const int sl = CPI > 1 ? lane % SL : lane;      // first slice of this lane
+  f32x4 acc[SPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
+  for (int v = 0; v < SPL; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lse_out = -INFINITY;
   if (m != -INFINITY) {
     float tot = 0.f;
-    for (int k = lane; k < n; k += 64) tot += fast_exp2((lp[k] - m) * kLog2e);
+#pragma unroll
+    for (int r = 0; r < MAXL; ++r) tot += fast_exp2((lv[r] - m) * kLog2e);
+    for (int k = lane + 64 * MAXL; k < n; k += 64) tot += fast_exp2((lp[k] - m) * kLog2e);
     tot = wave_sum(tot);
     const float inv = 1.0f / tot;
     lse_out = m + fast_log2(tot) * kLn2;
-    const float* op = c.o_part + row * c.max_chunks * D + lane * VPL;
-    for (int k = 0; k < n; ++k) {
-      const float lk = lp[k];
-      if (lk == -INFINITY) continue;    // empty chunk: weight 0, contents unused
-      const float w = fast_exp2((lk - m) * kLog2e) * inv;
+    const float* op = c.o_part + row * c.max_chunks * D;
+    for (int k0 = 0; k0 < n; k0 += CPI * BATCH) {
+      f32x4 x[BATCH][SPL];
+      float lk[BATCH];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) acc[v] = fmaf(w, op[(int64_t)k * D + v], acc[v]);
+      for (int u = 0; u < BATCH; ++u) {
+        const int k = k0 + CPI * u + co;
+        // the LSE of chunk k sits in lane k % 64, register k / 64 (< 256 chunks)
+        // (k / 64 is the same for the whole wave: 64 is a multiple of CPI)
+        float src = lv[0];
+#pragma unroll
+        for (int r = 1; r < MAXL; ++r)
+          if (((k0 + CPI * u) >> 6) == r) src = lv[r];
+        const float from_lane = __shfl(src, k & 63, 64);
+        lk[u] = k < n ? (k < 64 * MAXL ? from_lane : lp[k]) : -INFINITY;
+#pragma unroll
+        for (int v = 0; v < SPL; ++v)
+          x[u][v] = (k < n && lk[u] != -INFINITY)
+                        ? *reinterpret_cast<const f32x4*>(op + (int64_t)k * D + 4 * (sl + 64 * v))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        // empty chunk (LSE -inf): weight 0 and its contents are never read
+        const float w = lk[u] == -INFINITY ? 0.f : fast_exp2((lk[u] - m) * kLog2e) * inv;
+#pragma unroll
+        for (int v = 0; v < SPL; ++v) acc[v] += w * x[u][v];
+      }
     }
-  }
-  if constexpr (VPL == 1) {
-    dst[0] = (uint16_t)(pack_bf16(acc[0], 0.f) & 0xffffu);
-  } else {
+    // add the CPI lane groups that hold the same slice
 #pragma unroll
-    for (int v = 0; v < VPL; v += 2)
-      *reinterpret_cast<uint32_t*>(dst + v) = pack_bf16(acc[v], acc[v + 1]);
+    for (int sft = 32; sft >= SL && CPI > 1; sft >>= 1)
+#pragma unroll
+      for (int v = 0; v < SPL; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[v][e] += __shfl_xor(acc[v][e], sft, 64);
+  }
+  if (co == 0) {
+    uint16_t* dst = c.o + (((int64_t)b * c.Sq + i) * c.Hq + h) * D;
+#pragma unroll
+    for (int v = 0; v < SPL; ++v) {
+      u32x2 val = {pack_bf16(acc[v][0], acc[v][1]), pack_bf16(acc[v][2], acc[v][3])};
+      *reinterpret_cast<u32x2*>(dst + 4 * (sl + 64 * v)) = val;
+    }
   }
   if (c.lse != nullptr && lane == 0) c.lse[((int64_t)b * c.Hq + h) * c.Sq + i] = lse_out;
 }
@@ -155,7 +222,7 @@ hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
                 static_cast<uint16_t*>(d.o), d.lse, d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, c);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0, stream, c);
   return hipGetLastError();
 }
 

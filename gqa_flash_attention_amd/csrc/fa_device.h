@@ -69,10 +69,16 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4). The LDS
 // destination `lds_seg` must be the same for the whole wave: lane L's 16 bytes
-// land at lds_seg + 16 L bytes.
+// land at lds_seg + 16 L bytes. STREAM sets the non-temporal hint (nt): data
+// read once (a decode step's KV cache) streams past the caches; measured on
+// MI355X, it is what lets these copies approach HBM bandwidth (without it a
+// pure copy stream stalls near 4.7 TB/s).
+template <bool STREAM>
 __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_seg) {
+  constexpr int kNonTemporal = 2;
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_seg, 16, 0, 0);
+                                   (__attribute__((address_space(3))) void*)lds_seg, 16, 0,
+                                   STREAM ? kNonTemporal : 0);
 }
 
 // Scheduling hints (sched_group_barrier masks: 0x2 VALU, 0x8 MFMA, 0x100
@@ -101,9 +107,14 @@ __device__ __forceinline__ void sched_step() {
   sched_phase<N2, R2, a2, 0, 0>();
 }
 
-// Wait until this wave's outstanding global loads (including global -> LDS
-// copies) have completed: s_waitcnt vmcnt(0).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's global loads (including global -> LDS
+// copies, which complete in issue order) are outstanding: s_waitcnt vmcnt(N).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
+  constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
 
 // Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16). Within
 // each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows

@@ -92,9 +92,13 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
  *               [0, max_pages_per_seq * page_size].
  *   o           bf16 [B, Sq, Hq, D] output
  *   lse         fp32 [B, Hq, Sq] output, may be NULL
- *   num_pages   physical pages in the cache (block_table entries outside
- *               [0, num_pages) are read as masked keys, never dereferenced);
- *               ignored when block_table is NULL
+ *   num_pages   physical pages in the cache; ignored when block_table is
+ *               NULL. A block_table entry outside [0, num_pages) that covers
+ *               tokens below seq_lens[b] is a caller error that is not
+ *               detected: the entry is clamped into range, so every load
+ *               stays inside the cache, and that sequence's output is
+ *               unspecified. Entries past a sequence's last page are never
+ *               used.
  *   page_size   a power of two in [1, 65536]
  *   kv_chunk    tokens per split, > 0
  *   workspace   device buffer of at least

@@ -46,6 +46,9 @@ DECODE_GRID = [
     (2, 16, 32, 4, 128, 16, 512, (16, 512), 128, 0),    # 128 rows per KV head
     (2, 8, 64, 8, 128, 16, 1024, (8, 1024), 256, 100),  # sliding window
     (2, 2, 4, 1, 64, 64, 256, (0, 256), 64, 0),         # zero-length sequences possible
+    # over 16384 (sequence, KV head, chunk) slots: several chunks per workgroup
+    (64, 1, 16, 4, 64, 0, 4096, (1, 4096), 32, 0),
+    (40, 2, 8, 4, 128, 16, 4096, (1, 4096), 32, 0),
 ]
 
 
@@ -101,22 +104,33 @@ def test_paged_gather_bitexact():
     assert torch.equal(g2.view(torch.int16), r2.view(torch.int16))
 
 
-@pytest.mark.parametrize("D", [64, 128, 256, 512])
-def test_combine_against_oracle(D):
-    gen = torch.Generator().manual_seed(D)
-    B, Hq, Sq, C = 3, 4, 2, 7
+COMBINE_CASES = [(D, 7, (7, 5, 0)) for D in (64, 128, 256, 512)] + [
+    (128, 70, (70, 65, 1)),        # chunks past the first 64 (second LSE register)
+    (64, 300, (300, 257, 64)),     # more than 256 chunks (LSEs re-read from memory)
+    (512, 300, (299, 130, 256)),
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_CASES, ids=lambda c: "D{}_C{}".format(c[0], c[1]))
+def test_combine_against_oracle(case):
+    D, C, counts = case
+    gen = torch.Generator().manual_seed(D + C)
+    B, Hq, Sq = 3, 4, 2
     o_part = torch.randn(B, Hq, Sq, C, D, generator=gen)
     lse_part = 3 * torch.randn(B, Hq, Sq, C, generator=gen)
-    lse_part[0, 1, 0, 2] = float("-inf")            # an empty chunk
-    o_part[0, 1, 0, 2] = float("nan")               # whose contents must be ignored
+    empty = [(0, 1, 0, 2), (0, 3, 1, C - 2)]
+    for e in empty:
+        lse_part[e] = float("-inf")                 # an empty chunk
+        o_part[e] = float("nan")                    # whose contents must be ignored
     lse_part[1, 2, 1, :] = float("-inf")            # a row with no key at all
-    n_chunks = torch.tensor([7, 5, 0], dtype=torch.int32)
+    n_chunks = torch.tensor(counts, dtype=torch.int32)
     o, lse = fa.combine_lse(o_part.to(DEV), lse_part.to(DEV), n_chunks.to(DEV))
     torch.cuda.synchronize()
     op = o_part.clone()
-    op[0, 1, 0, 2] = 0.0
+    for e in empty:
+        op[e] = 0.0
     o_ref, lse_ref = oracle.combine_ref(op, lse_part, n_chunks.tolist())
-    assert_parity(o, lse, o_ref, lse_ref, f"combine D{D}")
+    assert_parity(o, lse, o_ref, lse_ref, f"combine D{D} C{C}")
 
 
 def test_decode_c3_full_size_sampled():
