@@ -68,10 +68,10 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
   if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0) return 0;
-  const int64_t chunks = n_chunks_for(max_seq_len, kv_chunk);
+  const int64_t slots = (int64_t)kSlotsPerChunk * n_chunks_for(max_seq_len, kv_chunk);
   const int64_t rows = (int64_t)B * Hq * Sq;
-  const size_t o_bytes = align256((size_t)(rows * chunks * D) * sizeof(float));
-  const size_t l_bytes = align256((size_t)(rows * chunks) * sizeof(float));
+  const size_t o_bytes = align256((size_t)(rows * slots * D) * sizeof(float));
+  const size_t l_bytes = align256((size_t)(rows * slots) * sizeof(float));
   return o_bytes + l_bytes;
 }
 
@@ -102,24 +102,28 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return FA_ERR_WORKSPACE;
   const int64_t max_chunks = n_chunks_for(max_len, kv_chunk);
+  const int64_t n_slots = (int64_t)kSlotsPerChunk * max_chunks;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
-  if ((int64_t)B * Hkv * ((rows + 31) / 32) * (max_chunks > 0 ? max_chunks : 1) > kMaxGrid)
+  // the split kernel counts tiles (at most one per 32 keys plus one per
+  // chunk, per block of 32 rows and KV head) in 32-bit integers
+  if ((int64_t)B * Hkv * ((rows + 31) / 32) * ((max_len + 31) / 32 + max_chunks) > INT32_MAX)
     return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;   // one combine workgroup per row
 
   const int64_t prow = (int64_t)B * Hq * Sq;
   float* o_part = static_cast<float*>(workspace);
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align256((size_t)(prow * max_chunks * D) * sizeof(float)));
+                                             align256((size_t)(prow * n_slots * D) * sizeof(float)));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (max_chunks > 0) {
     SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part,
                  B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
-                 (int)max_chunks, causal, window, scale};
+                 (int)n_slots, causal, window, scale};
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
-  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)max_chunks, o, lse, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)kSlotsPerChunk, (int)n_slots,
+                 o, lse, B, Sq, Hq, D};
   return to_status(launch_combine(cd, st));
 }
 
@@ -133,7 +137,7 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
   if (max_chunks > 0 && (!o_part || !lse_part || !aligned16(o_part))) return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
-  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, 1, max_chunks, o, lse, B, Sq, Hq, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
 }
 

@@ -40,9 +40,23 @@
 // partial S^T over its half of the contraction, the pair adds the two halves
 // through LDS (in the same order in both waves, so both hold bit-identical
 // scores and run identical softmax), and each then accumulates its half of O.
+//
+// Split-KV mode (decode and speculative verify) is bound by HBM bandwidth. A
+// persistent grid of as many workgroups as the GPU holds at once streams the
+// K/V tiles of all (sequence, block of rows) in one global order. The grid is
+// cut into sets of Hkv workgroups, member g of a set taking KV head g, and
+// each set takes an equal contiguous range of tiles, so every slot streams
+// until the end and none idles in a tail (the Stream-K way of balancing a
+// split reduction), and the Hkv workgroups of a set read the same token rows
+// ([.., Hkv, D] is token-major) side by side. Keys are cut into chunks of
+// kv_chunk tokens; every partial covers all or part of one chunk, tiles never
+// straddle a chunk, and a chunk cut by workgroup boundaries leaves one
+// partial per piece (slots 4c .. 4c + 3, the unused ones marked empty) that
+// the LSE combine merges like any others.
 #pragma once
 
 #include "fa_device.h"
+#include "fa_launch.h"
 
 namespace gqafa {
 
@@ -52,8 +66,8 @@ struct AttnArgs {
   const uint16_t* v;
   uint16_t* o;            // final output (prefill)
   float* lse;             // final LSE (prefill), may be null
-  float* o_part;          // split mode: fp32 [B, Hq, Sq, max_chunks, D]
-  float* lse_part;        // split mode: fp32 [B, Hq, Sq, max_chunks]
+  float* o_part;          // split mode: fp32 [B, Hq, Sq, n_slots, D]
+  float* lse_part;        // split mode: fp32 [B, Hq, Sq, n_slots]
   const int32_t* seq_lens;  // split mode: keys per sequence
   const int32_t* table;     // split mode: block table or null
   int page_shift, max_pages, num_pages;
@@ -63,8 +77,7 @@ struct AttnArgs {
   int causal, window;
   float sl2;              // scale * log2(e)
   int n_rb;               // row blocks per (b, g)
-  int chunk, max_chunks;  // split mode: keys per partial, partial slots per row
-  int cpw, n_cg;          // split mode: chunks per workgroup, chunk groups per row block
+  int chunk, n_slots;     // split mode: keys per chunk, partial slots per row (kSlotsPerChunk per chunk)
 };
 
 // Spread a 1-D grid over the 8 XCDs so that logical neighbours (row blocks of
@@ -101,7 +114,50 @@ __device__ __forceinline__ int swz_v(int row) {
   else return rr << 1;
 }
 
-template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, bool MULTI, int WPE>
+// The keys any row of one block of rows may attend to, as tiles of BN keys
+// laid out chunk by chunk: tile k of chunk c starts at key c * chunk + k * BN
+// and never crosses the chunk's end. Chunks c_lo .. c_hi hold visible keys;
+// the first holds tiles k0 .. tpc - 1 (tpc tiles per chunk), the last tiles
+// 0 .. k1 (k0 .. k1 when they are the same chunk).
+struct RowSpan {
+  int c_lo, k0, c_hi, k1;
+  int nt;                    // tiles in all (0: no visible key)
+};
+template <int BN, int BM>
+__device__ __forceinline__ RowSpan row_span(const AttnArgs& a, int len, int rb, int tpc) {
+  RowSpan s{0, 0, 0, 0, 0};
+  const int rows = a.Sq * a.G;
+  const int r_lo = rb * BM, r_hi = min(r_lo + BM, rows);
+  const int shift = len - a.Sq;               // bottom-right causal alignment
+  int lo = 0, hi = len;
+  if (a.causal) {
+    hi = min(hi, (r_hi - 1) / a.G + shift + 1);
+    if (a.window > 0) lo = max(lo, r_lo / a.G + shift - a.window + 1);
+  }
+  if (hi <= lo) return s;
+  s.c_lo = lo / a.chunk;
+  s.c_hi = (hi - 1) / a.chunk;
+  s.k0 = (lo - s.c_lo * a.chunk) / BN;
+  s.k1 = (hi - 1 - s.c_hi * a.chunk) / BN;
+  s.nt = s.c_lo == s.c_hi ? s.k1 - s.k0 + 1 : (tpc - s.k0) + (s.c_hi - s.c_lo - 1) * tpc + s.k1 + 1;
+  return s;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) x += __shfl_xor(x, s, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int y = __shfl_up(x, s, 64);
+    if (lane >= s) x += y;
+  }
+  return x;
+}
+
+template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
@@ -115,10 +171,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   constexpr int NDB = D / 32 / DS;            // 32-wide d blocks of O per wave
   constexpr int NQC = D / 16 / DS;            // 16-wide d steps of Q K^T per wave
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tile buffers per operand");
-  static_assert(SPLIT || !MULTI, "several chunks per workgroup only in split mode");
-  // block-table entries staged in LDS (none at D = 512, where the tile ring
-  // and the score exchange fill LDS)
-  constexpr int TAB = (PAGED && SPLIT && D < 512) ? 2048 : 0;
+  // Split mode: a window of block-table entries staged in LDS (none at
+  // D = 512, where the tile ring and the score exchange fill LDS). The
+  // contiguous-cache kernel reserves the same space, so both kernels hold
+  // the same number of workgroups per CU and split the work identically.
+  constexpr int TAB = (SPLIT && D < 512) ? 512 : 0;
 
   // A ring of NBUF tile buffers per operand, each its own object: the copies
   // into one never alias reads of another, so no read waits on a copy it does
@@ -136,6 +193,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   if constexpr (TAB > 0) {
     __shared__ int sT_buf[TAB > 0 ? TAB : 1];
     sT = sT_buf;
+    asm volatile("" ::"v"(sT_buf));           // keeps the reservation in the dense kernel
   }
   // partial scores exchanged by the waves of a D split, [slot][wave][value][lane]
   __shared__ float sX[DS > 1 ? 2 : 1][DS > 1 ? NW : 1][DS > 1 ? NKB * 16 : 1][64];
@@ -148,93 +206,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   const int rg = wave / DS;    // row group (32 rows) of this wave
   const int dh = wave % DS;    // which half of the head dim this wave holds
 
-  // ---- work item -------------------------------------------------------
-  int b, g, rb, cg = 0;
-  if constexpr (SPLIT) {
-    // KV head fastest: the workgroups reading the Hkv head slices of one
-    // token range run side by side, so together they read whole token rows
-    // ([.., Hkv, D] is token-major) instead of scattered head slices
-    int L = blockIdx.x;
-    g = L % a.Hkv;
-    L /= a.Hkv;
-    rb = L % a.n_rb;
-    L /= a.n_rb;
-    cg = L % a.n_cg;
-    b = L / a.n_cg;
-  } else {
-    const int n = a.B * a.Hkv * a.n_rb;
-    const int L = xcd_remap(blockIdx.x, n);
-    const int bg = L / a.n_rb;
-    rb = a.n_rb - 1 - (L % a.n_rb);   // heaviest causal row blocks first
-    b = bg / a.Hkv;
-    g = bg % a.Hkv;
-  }
-
-  int n_keys;
-  int c0 = 0, c1 = 1;   // split mode: this workgroup's partials [c0, c1)
-  if constexpr (SPLIT) {
-    const int64_t cap = (int64_t)a.max_pages << a.page_shift;
-    int64_t sl = a.seq_lens[b];
-    sl = sl < 0 ? 0 : (sl > cap ? cap : sl);
-    n_keys = (int)sl;
-    const int nch = (int)((sl + a.chunk - 1) / a.chunk);
-    c0 = cg * a.cpw;
-    if (c0 >= nch) return;  // past the end: the merge reads no partial here
-    c1 = min(c0 + a.cpw, nch);
-  } else {
-    n_keys = a.skv;
-  }
-
-  const int rows = a.Sq * a.G;
-  const int r_lo = rb * BM;
-  const int r_hi = min(r_lo + BM, rows);
-  const int shift = n_keys - a.Sq;             // bottom-right causal alignment
-  const int pmin = r_lo / a.G + shift;
-  const int pmax = (r_hi - 1) / a.G + shift;
-
-  // keys this workgroup may need: [kv_lo, kv_hi), inside the split [kb0, ke)
-  int kb0 = 0, ke = n_keys;
-  if constexpr (SPLIT) {
-    kb0 = c0 * a.chunk;
-    ke = (int)min((int64_t)n_keys, (int64_t)c1 * a.chunk);
-  }
-  int kv_lo = kb0, kv_hi = ke;
-  if (a.causal) {
-    kv_hi = min(kv_hi, pmax + 1);
-    if (a.window > 0) kv_lo = max(kv_lo, pmin - a.window + 1);
-  }
-  const int t_start = kb0 + ((max(kv_lo, kb0) - kb0) / BN) * BN;
-  const int n_tiles = kv_hi > kv_lo ? (kv_hi - t_start + BN - 1) / BN : 0;
-
-  // ---- this lane's query row ---------------------------------------------
-  const int wr_lo = r_lo + 32 * rg;
-  const bool wave_rows = wr_lo < r_hi;
-  const int wr_hi = min(wr_lo + 32, r_hi);
-  const int wpmin = wr_lo / a.G + shift;
-  const int wpmax = (wr_hi - 1) / a.G + shift;
-  const int r = wr_lo + j;
-  const bool row_ok = r < r_hi;
-  const int qi = row_ok ? r / a.G : 0;
-  const int qh = g * a.G + (row_ok ? r % a.G : 0);
-  const int p = qi + shift;                    // absolute position of the row
-
-  bf16x8 qf[NQC];
-  {
-    const int64_t qoff = (((int64_t)b * a.Sq + qi) * a.Hq + qh) * D + 8 * hl + dh * (D / DS);
-#pragma unroll
-    for (int c = 0; c < NQC; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
-      qf[c] = as_bf16x8(w);
-    }
-  }
-
-  // ---- staging: global -> LDS ------------------------------------------
+  // ---- staging geometry: global -> LDS ---------------------------------------
   // Segment s (1 KiB) of a tile holds chunk positions 64 s .. 64 s + 63 of
   // the row-major tile: lane L writes position 64 s + L = row * KCH + pc,
   // holding logical chunk pc ^ swizzle(row) of that key row.
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const int64_t head_off = (int64_t)g * D;
   // Per-lane segment geometry. With few segments per wave it is kept in
   // registers; with many (large head dims, few waves) it is recomputed at
   // each copy, which costs a few integer operations instead of 3 registers
@@ -261,40 +237,37 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       voff[i] = seg_voff(i);
     }
   }
-  const uint16_t* kseq = a.k + head_off;
-  const uint16_t* vseq = a.v + head_off;
-  if constexpr (!PAGED) {
-    kseq += (int64_t)b * a.slots * row_stride;
-    vseq += (int64_t)b * a.slots * row_stride;
-  }
 
-  // Paged split: the workgroup's slice of the block table (clamped into
-  // [0, num_pages)) is staged in LDS once, so no tile copy waits on a table
-  // load; a slice longer than the staging area is read from global memory.
-  int p0 = 0;
-  bool tab_lds = false;
-  if constexpr (PAGED && SPLIT) {
-    p0 = kb0 >> a.page_shift;
-    const int np = ke > kb0 ? ((ke - 1) >> a.page_shift) - p0 + 1 : 0;
-    tab_lds = TAB > 0 && np <= TAB;
-    if (tab_lds) {
-      for (int i = tid; i < np; i += NW * 64) {
-        const int page = a.table[(int64_t)b * a.max_pages + p0 + i];
-        sT[i] = min(max(page, 0), a.num_pages - 1);
-      }
+  // Paged split: a window of one sequence's block-table row, clamped into
+  // [0, num_pages), staged in LDS so that no tile copy waits on a table
+  // load. A tile outside the window restages it (all waves together).
+  int tw_b = -1, tw_p0 = 0;
+  auto stage_table = [&](int b_t, int pf) {
+    __syncthreads();                          // every wave is done with the old window
+    const int np = min(TAB, a.max_pages - pf);
+    for (int i = tid; i < np; i += NW * 64) {
+      const int page = a.table[(int64_t)b_t * a.max_pages + pf + i];
+      sT[i] = min(max(page, 0), a.num_pages - 1);
     }
     __syncthreads();
-  }
+    tw_b = b_t;
+    tw_p0 = pf;
+  };
 
-  // Keys past the end of the range are clamped onto its last key: their
-  // scores are masked and their V rows get weight exactly 0, so the data read
-  // there never matters (and is always finite in-range data). A block-table
-  // entry outside [0, num_pages) is clamped into range: every load stays
-  // inside the cache.
-  auto issue = [&](int tb, bool is_v, uint16_t* dst) {
-    const uint16_t* seq = is_v ? vseq : kseq;
-    const int lim = ke - 1 - tb;              // last valid row of this tile
+  // Copy one operand of the tile of keys [tb, tb + BN) of a sequence whose
+  // keys end at ke_t (exclusive) into dst. kv_base is the K or V cache at
+  // this KV head (and, for a contiguous cache, at this sequence). Keys past
+  // ke_t are clamped onto its last key: their scores are masked and their V
+  // rows get weight exactly 0, so the data read there never matters (and is
+  // always finite in-range data). A block-table entry outside [0, num_pages)
+  // is clamped into range: every load stays inside the cache.
+  auto issue = [&](int tb, int ke_t, const uint16_t* kv_base, int b_t, bool is_v, uint16_t* dst) {
+    const int lim = ke_t - 1 - tb;            // last valid row of this tile
     const bool tail = lim < BN - 1;           // uniform
+    if constexpr (PAGED && TAB > 0) {
+      const int pf = tb >> a.page_shift, pl = (tb + min(lim, BN - 1)) >> a.page_shift;
+      if (b_t != tw_b || pf < tw_p0 || pl >= tw_p0 + TAB) stage_table(b_t, pf);
+    }
 #pragma unroll
     for (int i = 0; i < SEGW; ++i) {
       const int row = KEEP_SEG ? srow[i] : seg_row(i);
@@ -303,26 +276,62 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       if constexpr (PAGED) {
         const int t = tb + min(row, lim);
         int page;
-        if (tab_lds) {
-          page = sT[(t >> a.page_shift) - p0];
+        if constexpr (TAB > 0) {
+          page = sT[(t >> a.page_shift) - tw_p0];
         } else {
-          page = a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
+          page = a.table[(int64_t)b_t * a.max_pages + (t >> a.page_shift)];
           page = min(max(page, 0), a.num_pages - 1);
         }
         const int64_t base = ((((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1))) -
                               row) * row_stride;
-        src = reinterpret_cast<const char*>(seq + base) + off0;
+        src = reinterpret_cast<const char*>(kv_base + base) + off0;
       } else {
         // uniform tile base + 32-bit per-lane byte offset
         uint32_t o = off0;
         if (tail && row > lim) o -= 2u * (uint32_t)((row - lim) * (int)row_stride);
-        src = reinterpret_cast<const char*>(seq + (int64_t)tb * row_stride) + o;
+        src = reinterpret_cast<const char*>(kv_base + (int64_t)tb * row_stride) + o;
       }
       dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
     }
   };
-  auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, false, dst); };
-  auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, true, dst); };
+  // K and V cache bases of (sequence b, KV head g)
+  auto kv_bases = [&](int b_t, int g_t, const uint16_t*& kb_out, const uint16_t*& vb_out) {
+    int64_t off = (int64_t)g_t * D;
+    if constexpr (!PAGED) off += (int64_t)b_t * a.slots * row_stride;
+    kb_out = a.k + off;
+    vb_out = a.v + off;
+  };
+
+  // ---- the rows being worked on: one block of rows of one (b, KV head) ------
+  // In split mode they change as the workgroup moves through its tiles.
+  int b = 0;
+  int p = 0, wpmin = 0, wpmax = 0, qi = 0, qh = 0;
+  bool row_ok = false;
+  int ke = 0;                  // end (exclusive) of the keys the current tile may hold
+  bf16x8 qf[NQC];
+  auto set_rows = [&](int b_, int g_, int rb_, int n_keys) {
+    b = b_;
+    const int rows = a.Sq * a.G;
+    const int r_lo = rb_ * BM;
+    const int r_hi = min(r_lo + BM, rows);
+    const int shift = n_keys - a.Sq;           // bottom-right causal alignment
+    const int wr_lo = r_lo + 32 * rg;
+    const int wr_hi = min(wr_lo + 32, r_hi);
+    wpmin = wr_lo / a.G + shift;
+    wpmax = (wr_hi - 1) / a.G + shift;
+    const int r = wr_lo + j;
+    row_ok = r < r_hi;
+    qi = row_ok ? r / a.G : 0;
+    qh = g_ * a.G + (row_ok ? r % a.G : 0);
+    p = qi + shift;                            // absolute position of this lane's row
+    const int64_t qoff = (((int64_t)b_ * a.Sq + qi) * a.Hq + qh) * D + 8 * hl + dh * (D / DS);
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
+      qf[c] = as_bf16x8(w);
+    }
+  };
 
   // ---- LDS read addresses --------------------------------------------------
   // K (A operand of S^T): row 32 kb + j, logical chunk 2 (c + dh NQC) + hl.
@@ -481,113 +490,386 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // exp per score, one add per score and one pack per pair
   constexpr int kExpValuPerTile = NKB * 16 * 3 + NKB * 8;
 
-  // ---- main loop, software-pipelined -----------------------------------------
-  // Step t: the scores of tile t are already in registers. After the barrier
-  // (tile t+1's K and tile t's V have landed in LDS, and every wave is done
-  // with step t-1), the wave starts the copies of K(t+NBUF) and V(t+NBUF-1)
-  // into the buffers step t-1 released, runs the S^T MFMAs of tile t+1 while
-  // the VALU exponentiates tile t, then accumulates O with tile t's V. The
-  // MFMA work of S(t+1) overlaps the softmax of tile t inside one wave, and
-  // NBUF-1 tiles of copies stay in flight. The copies of one step (K(t+1+j),
-  // V(t+j)) form a group; the wait before step t lets the groups issued after
-  // group t stay outstanding. Buffer indices are compile-time constants in
-  // the unrolled ring.
   auto kbuf = [&](int i) -> uint16_t* { return i == 0 ? sK0 : i == 1 ? sK1 : i == 2 ? sK2 : sK3; };
   auto vbuf = [&](int i) -> uint16_t* { return i == 0 ? sV0 : i == 1 ? sV1 : i == 2 ? sV2 : sV3; };
-  constexpr int GROUP = 2 * SEGW;                         // copy instructions per group
-  constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
-  constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
 
-  // split mode: finish the partial of chunk c with the current state, then
-  // start the next chunk from scratch
-  int cur_chunk = SPLIT ? t_start / a.chunk : 0;
-  auto write_partial = [&](int c) {
-    const float l_tot = pair_sum(l_run);
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : fast_rcp(l_tot);
-    const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
-    if (row_ok) {
-      const int64_t prow = (((int64_t)b * a.Hq + qh) * a.Sq + qi) * a.max_chunks + c;
-      float* dst = a.o_part + prow * D;
+  if constexpr (SPLIT) {
+    // ======================= split-KV: persistent Stream-K =====================
+    const int C = a.chunk;
+    const int tpc = (C + BN - 1) / BN;          // tiles per chunk
+    const int W = gridDim.x, w = blockIdx.x;
+    const int64_t cap = (int64_t)a.max_pages << a.page_shift;
+    auto clamp_len = [&](int v) -> int { return (int)min(max((int64_t)v, (int64_t)0), cap); };
+    // tiles of every block of rows of one sequence (per KV head)
+    auto seq_tiles = [&](int len) -> int {
+      int n = 0;
+      for (int r = 0; r < a.n_rb; ++r) n += row_span<BN, BM>(a, len, r, tpc).nt;
+      return n;
+    };
+
+    // Partial slot of query row (qi, head qh) of sequence b.
+    auto slot_index = [&](int s_) -> int64_t {
+      return (((int64_t)b * a.Hq + qh) * a.Sq + qi) * a.n_slots + s_;
+    };
+    // Normalised partial output and LSE of the current state into slot s_.
+    auto write_partial = [&](int s_) {
+      const float l_tot = pair_sum(l_run);
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : fast_rcp(l_tot);
+      const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
+      if (row_ok) {
+        const int64_t prow = slot_index(s_);
+        float* dst = a.o_part + prow * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
-          f32x4 val = {oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv,
-                       oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv};
-          *reinterpret_cast<f32x4*>(dst + d0) = val;
+          for (int rr = 0; rr < 4; ++rr) {
+            const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
+            f32x4 val = {oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv,
+                         oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv};
+            *reinterpret_cast<f32x4*>(dst + d0) = val;
+          }
+        if (hl == 0 && dh == 0) a.lse_part[prow] = lse_v;
+      }
+    };
+    // Slots [s0, s1) of the current rows hold no key (LSE -inf; the combine
+    // never reads their O).
+    auto write_empty = [&](int s0, int s1) {
+      if (row_ok && hl == 0 && dh == 0)
+        for (int s_ = s0; s_ < s1; ++s_) a.lse_part[slot_index(s_)] = -INFINITY;
+    };
+    auto reset_state = [&]() {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    };
+
+    // ---- total tile count T, lane-parallel over sequences -------------------
+    // The lengths of sequences bc0 + lane + 64 r stay in lane registers: the
+    // tile iterators read them with readlane, so moving to the next sequence
+    // costs no memory access (a global load would wait for every copy in
+    // flight).
+    int lenc[4] = {0, 0, 0, 0};
+    int bc0 = 0;
+    int T = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 256) {
+      int lv[4];
+      int part_sum = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int bb = b0 + lane + 64 * r;
+        lv[r] = bb < a.B ? clamp_len(a.seq_lens[bb]) : 0;
+        part_sum += bb < a.B ? seq_tiles(lv[r]) : 0;
+      }
+      if (b0 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lenc[r] = lv[r];
+      }
+      T += wave_sum_i32(part_sum);
+    }
+    auto len_of = [&](int bb) -> int {
+      const int d = bb - bc0;
+      if (d >= 0 && d < 256) {
+        const int r = d >> 6, l = d & 63;
+        const int v = r == 0 ? lenc[0] : r == 1 ? lenc[1] : r == 2 ? lenc[2] : lenc[3];
+        return __builtin_amdgcn_readlane(v, l);
+      }
+      return __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[bb]));
+    };
+
+    // ---- block rows with no visible key: every slot of their rows is empty ---
+    for (int bb = w; bb < a.B; bb += W) {
+      const int len = len_of(bb);
+      const int nch = (int)(((int64_t)len + C - 1) / C);
+      if (nch == 0) continue;
+      for (int r = 0; r < a.n_rb; ++r) {
+        if (row_span<BN, BM>(a, len, r, tpc).nt > 0) continue;
+        for (int gg = 0; gg < a.Hkv; ++gg) {
+          set_rows(bb, gg, r, len);
+          write_empty(0, kSlotsPerChunk * nch);
         }
-      if (hl == 0 && dh == 0) a.lse_part[prow] = lse_v;
-    }
-  };
-  auto reset_state = [&]() {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    m_run = -INFINITY;
-    l_run = 0.f;
-  };
-
-  f32x16 sc[NKB];
-  if (n_tiles > 0) {
-    issue_k(t_start, kbuf(0));
-#pragma unroll
-    for (int jj = 0; jj < NBUF - 1; ++jj) {
-      if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
-      if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
-    }
-    if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
-    __syncthreads();
-    scores(kbuf(0), sc);
-    publish(sc, 0);
-  }
-  auto step = [&](int it, int u) {
-    const int tb = t_start + it * BN;
-    if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
-    __syncthreads();
-    if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
-    if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
-    if constexpr (SPLIT && MULTI) {
-      if (tb / a.chunk != cur_chunk) {      // uniform: first tile of the next chunk
-        write_partial(cur_chunk);
-        reset_state();
-        cur_chunk = tb / a.chunk;
       }
     }
-    combine_partner(sc, it & 1);
-    const float nb = prepare(sc, tb);
-    f32x16 sn[NKB];
-    scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
-    u32x4 pf[NKS];
-    exponentiate(sc, nb, pf);
-    publish(sn, (it + 1) & 1);
-    accumulate(vbuf(u), pf);
-    // one schedule for the whole step: S(t+1) MFMAs each followed by the
-    // next K read and a share of tile t's exponentiation, then the PV MFMAs
-    // each followed by the next two V^T reads
-    sched_step<NKB * NQC, 1, NDB * NKS, 2, (D >= 512 ? 2 : 4), kExpValuPerTile / (NKB * NQC)>();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
-  };
-  for (int it = 0; it < n_tiles; it += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      if (it + u >= n_tiles) break;
-      step(it + u, u);
-    }
-  }
 
-  // ---- epilogue ----------------------------------------------------------
-  if constexpr (SPLIT) {
-    // the chunk of the last tile holds the running state; every other
-    // partial of [c0, c1) that no tile reached (wholly masked) is empty
-    const int c_last = n_tiles > 0 ? (t_start + (n_tiles - 1) * BN) / a.chunk : -1;
-    const int c_first = n_tiles > 0 ? t_start / a.chunk : 0;
-    if (n_tiles > 0) write_partial(c_last);
-    reset_state();
-    for (int c = c0; c < c1; ++c)
-      if (n_tiles == 0 || c < c_first || c > c_last) write_partial(c);
+    // ---- this workgroup's KV head and tile range [x0, x1) -------------------
+    // (the grid is a multiple of Hkv workgroups)
+    const int g_w = w % a.Hkv;
+    const int sets = W / a.Hkv;
+    // a chunk (at most tpc tiles) must meet at most SPC ranges
+    constexpr int SPC = kSlotsPerChunk;
+    const int per_min = max((tpc - 1 + SPC - 2) / (SPC - 1), 1);
+    const int per = (int)max(((int64_t)T + sets - 1) / sets, (int64_t)per_min);
+    const int64_t x0l = (int64_t)(w / a.Hkv) * per;
+    if (x0l >= T) return;
+    const int x0 = (int)x0l;
+    const int x1 = (int)min(x0l + per, (int64_t)T);
+    const int n_loc = x1 - x0;
+
+    // Tile iterator over the global order (sequence, block of rows, tile);
+    // all fields are uniform.
+    struct It {
+      int b, len, rb, i, nt, c, k, c_lo, k0, c_hi, k1;
+    };
+    auto it_span = [&](It& t, const RowSpan& sp) {
+      t.nt = sp.nt; t.c_lo = sp.c_lo; t.k0 = sp.k0; t.c_hi = sp.c_hi; t.k1 = sp.k1;
+      t.i = 0; t.c = sp.c_lo; t.k = sp.k0;
+    };
+    auto it_next = [&](It& t) {
+      if (++t.i < t.nt) {
+        if (++t.k == tpc) { t.k = 0; ++t.c; }
+        return;
+      }
+      for (;;) {
+        if (++t.rb == a.n_rb) {
+          t.rb = 0;
+          if (++t.b >= a.B) { t.nt = 0; return; }   // past the last tile
+          t.len = len_of(t.b);
+        }
+        const RowSpan sp = row_span<BN, BM>(a, t.len, t.rb, tpc);
+        if (sp.nt > 0) { it_span(t, sp); return; }
+      }
+    };
+
+    // ---- locate tile x0 -------------------------------------------------------
+    It cu;
+    {
+      int bx = 0, sx = 0, base = 0;
+      bool found = false;
+      for (int b0 = 0; b0 < a.B && !found; b0 += 256) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int bb = b0 + lane + 64 * r;
+          const int len = b0 == 0 ? lenc[r] : (bb < a.B ? clamp_len(a.seq_lens[bb]) : 0);
+          const int t = bb < a.B ? seq_tiles(len) : 0;
+          const int incl = wave_incl_scan_i32(t, lane) + base;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(!found && bb < a.B && incl > x0);
+          if (m != 0) {
+            const int L = __builtin_ctzll(m);
+            bx = b0 + 64 * r + L;
+            sx = __builtin_amdgcn_readlane(incl - t, L);
+            found = true;
+          }
+          base = __builtin_amdgcn_readlane(incl, 63);
+        }
+      }
+      if (!found) return;                      // (x0 < T always finds it)
+      cu.b = bx;
+      cu.len = len_of(bx);
+      int o = x0 - sx;
+      RowSpan sp{0, 0, 0, 0, 0};
+      for (cu.rb = 0; cu.rb < a.n_rb; ++cu.rb) {
+        sp = row_span<BN, BM>(a, cu.len, cu.rb, tpc);
+        if (o < sp.nt) break;
+        o -= sp.nt;
+      }
+      if (cu.rb == a.n_rb || sp.nt == 0) return;
+      it_span(cu, sp);
+      cu.i = o;
+      if (cu.i < tpc - cu.k0) {
+        cu.k = cu.k0 + cu.i;
+      } else {
+        const int i2 = cu.i - (tpc - cu.k0);
+        cu.c = cu.c_lo + 1 + i2 / tpc;
+        cu.k = i2 % tpc;
+      }
+    }
+    auto tile_tb = [&](const It& t) -> int { return t.c * C + t.k * BN; };
+    auto tile_ke = [&](const It& t) -> int { return (int)min((int64_t)(t.c + 1) * C, (int64_t)t.len); };
+    auto last_of_chunk = [&](const It& t) -> bool { return t.c == t.c_hi ? t.k == t.k1 : t.k == tpc - 1; };
+    auto n_chunks = [&](const It& t) -> int { return (int)(((int64_t)t.len + C - 1) / C); };
+
+    set_rows(cu.b, g_w, cu.rb, cu.len);
+    // a row's first tile also marks the chunks before its visible keys empty
+    if (cu.i == 0) write_empty(0, SPC * cu.c_lo);
+    // Global index of the current chunk's first tile; the piece of the chunk
+    // in range r (ranges are [r per, (r + 1) per)) fills slot SPC c + r - r0,
+    // with r0 the range of that first tile.
+    int cfx = x0 - (cu.k - (cu.c == cu.c_lo ? cu.k0 : 0));
+    int part = x0 / per - cfx / per;
+
+    // ---- copy pipeline --------------------------------------------------------
+    // The loop keeps as many copies in flight as the ring holds instead of
+    // overlapping MFMA and softmax. Each buffer is refilled as soon as its
+    // tile is consumed: K(t + NBUF) right after the scores of tile t,
+    // V(t + NBUF) right after its PV product, so at every wait 2 (NBUF - 1) of
+    // the 2 NBUF buffers are still being filled. Copy order: K0 V0 K1 V1 ..
+    // K(NBUF-1) V(NBUF-1), then per step t V(t + NBUF - 1) (refilling tile
+    // t-1's V buffer) and K(t + NBUF). The tiles in flight may belong to later
+    // rows: the V copy of step t is for the tile whose K was copied one step
+    // earlier, so one descriptor (key start, key end, V base, sequence) of
+    // that tile is kept.
+    constexpr int AHEAD_CP = 2 * (NBUF - 1) * SEGW < 63 ? 2 * (NBUF - 1) * SEGW : 63;
+    It pf = cu;
+    int d_tb = 0, d_ke = 0, d_b = 0;
+    const uint16_t* d_vb = nullptr;
+    auto issue_next_k = [&](uint16_t* dst) {   // K of the prefetch iterator's tile
+      const uint16_t* kb_;
+      kv_bases(pf.b, g_w, kb_, d_vb);
+      d_tb = tile_tb(pf);
+      d_ke = tile_ke(pf);
+      d_b = pf.b;
+      issue(d_tb, d_ke, kb_, d_b, false, dst);
+    };
+#pragma unroll
+    for (int jj = 0; jj < NBUF; ++jj) {
+      if (jj < n_loc) {
+        issue_next_k(kbuf(jj));
+        issue(d_tb, d_ke, d_vb, d_b, true, vbuf(jj));
+        if (jj + 1 < n_loc) it_next(pf);
+      }
+    }
+    auto sstep = [&](int it, int u) {
+      const bool deep = it + NBUF - 1 < n_loc;   // uniform: a full ring behind this tile
+      // K(t) landed in every wave's share; every wave is done with the PV
+      // product of tile t-1, whose V buffer is refilled next
+      if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
+      __syncthreads();
+      if (it >= 1 && it + NBUF - 1 < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf((u + NBUF - 1) % NBUF));
+      const int tb = tile_tb(cu);
+      ke = tile_ke(cu);
+      f32x16 sc[NKB];
+      scores(kbuf(u), sc);
+      if constexpr (DS > 1) {
+        publish(sc, it & 1);
+        __syncthreads();
+        combine_partner(sc, it & 1);
+      }
+      const float nb = prepare(sc, tb);
+      u32x4 pv[NKS];
+      exponentiate(sc, nb, pv);
+      // V(t) landed; every wave is done with K(t), whose buffer is refilled
+      if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
+      __syncthreads();
+      if (it + NBUF < n_loc) {
+        issue_next_k(kbuf(u));
+        if (it + NBUF + 1 < n_loc) it_next(pf);
+      }
+      accumulate(vbuf(u), pv);
+
+      // ---- after the tile: close the partial if its chunk or rows end here ---
+      // The rows change exactly after their last tile; inside the rows the
+      // chunk changes exactly after its last tile.
+      const bool range_end = it + 1 == n_loc;
+      const bool rows_end = cu.i == cu.nt - 1;
+      const bool chunk_end = last_of_chunk(cu);
+      if (range_end || chunk_end) {
+        write_partial(SPC * cu.c + part);
+        if (part == 0) {
+          // the range holding the chunk's first tile marks the slots its
+          // pieces do not use empty
+          const int last = (cu.c == cu.c_hi ? cu.k1 : tpc - 1) - (cu.c == cu.c_lo ? cu.k0 : 0);
+          const int pieces = (cfx + last) / per - cfx / per + 1;
+          write_empty(SPC * cu.c + pieces, SPC * cu.c + SPC);
+        }
+        // the rows' last tile marks the chunks after their visible keys empty
+        if (rows_end) write_empty(SPC * (cu.c_hi + 1), SPC * n_chunks(cu));
+        reset_state();
+        part = 0;
+        cfx = x0 + it + 1;                       // the next tile starts a chunk
+      }
+      if (!range_end) {
+        it_next(cu);
+        if (rows_end) {
+          set_rows(cu.b, g_w, cu.rb, cu.len);
+          write_empty(0, SPC * cu.c_lo);
+        }
+      }
+    };
+    for (int it = 0; it < n_loc; it += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        if (it + u >= n_loc) break;
+        sstep(it + u, u);
+      }
+    }
   } else {
+    // ======================= prefill: one block of rows per workgroup ==========
+    const int n = a.B * a.Hkv * a.n_rb;
+    const int L = xcd_remap(blockIdx.x, n);
+    const int bg = L / a.n_rb;
+    const int rb = a.n_rb - 1 - (L % a.n_rb);   // heaviest causal row blocks first
+    const int bq = bg / a.Hkv;
+    const int g = bg % a.Hkv;
+    const int n_keys = a.skv;
+    ke = n_keys;
+    const int rows = a.Sq * a.G;
+    const int r_lo = rb * BM;
+    const int r_hi = min(r_lo + BM, rows);
+    const int shift = n_keys - a.Sq;
+    const int pmin = r_lo / a.G + shift;
+    const int pmax = (r_hi - 1) / a.G + shift;
+    int kv_lo = 0, kv_hi = n_keys;
+    if (a.causal) {
+      kv_hi = min(kv_hi, pmax + 1);
+      if (a.window > 0) kv_lo = max(kv_lo, pmin - a.window + 1);
+    }
+    const int t_start = (max(kv_lo, 0) / BN) * BN;
+    const int n_tiles = kv_hi > kv_lo ? (kv_hi - t_start + BN - 1) / BN : 0;
+    set_rows(bq, g, rb, n_keys);
+    const uint16_t* kseq;
+    const uint16_t* vseq;
+    kv_bases(bq, g, kseq, vseq);
+    auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, n_keys, kseq, bq, false, dst); };
+    auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, n_keys, vseq, bq, true, dst); };
+
+    // ---- main loop, software-pipelined ---------------------------------------
+    // Step t: the scores of tile t are already in registers. After the
+    // barrier (tile t+1's K and tile t's V have landed in LDS, and every wave
+    // is done with step t-1), the wave starts the copies of K(t+NBUF) and
+    // V(t+NBUF-1) into the buffers step t-1 released, runs the S^T MFMAs of
+    // tile t+1 while the VALU exponentiates tile t, then accumulates O with
+    // tile t's V. The MFMA work of S(t+1) overlaps the softmax of tile t
+    // inside one wave, and NBUF-1 tiles of copies stay in flight. The copies
+    // of one step (K(t+1+j), V(t+j)) form a group; the wait before step t
+    // lets the groups issued after group t stay outstanding. Buffer indices
+    // are compile-time constants in the unrolled ring.
+    constexpr int GROUP = 2 * SEGW;                         // copy instructions per group
+    constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
+    constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
+    f32x16 sc[NKB];
+    if (n_tiles > 0) {
+      issue_k(t_start, kbuf(0));
+#pragma unroll
+      for (int jj = 0; jj < NBUF - 1; ++jj) {
+        if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
+        if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
+      }
+      if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
+      __syncthreads();
+      scores(kbuf(0), sc);
+      publish(sc, 0);
+    }
+    auto step = [&](int it, int u) {
+      const int tb = t_start + it * BN;
+      if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
+      __syncthreads();
+      if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
+      if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
+      combine_partner(sc, it & 1);
+      const float nb = prepare(sc, tb);
+      f32x16 sn[NKB];
+      scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
+      u32x4 pf[NKS];
+      exponentiate(sc, nb, pf);
+      publish(sn, (it + 1) & 1);
+      accumulate(vbuf(u), pf);
+      // one schedule for the whole step: S(t+1) MFMAs each followed by the
+      // next K read and a share of tile t's exponentiation, then the PV MFMAs
+      // each followed by the next two V^T reads
+      sched_step<NKB * NQC, 1, NDB * NKS, 2, (D >= 512 ? 2 : 4), kExpValuPerTile / (NKB * NQC)>();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+    };
+    for (int it = 0; it < n_tiles; it += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        if (it + u >= n_tiles) break;
+        step(it + u, u);
+      }
+    }
+
+    // ---- epilogue ------------------------------------------------------------
     const float l_tot = pair_sum(l_run);
     if (!row_ok) return;
     const bool empty = !(l_tot > 0.f);

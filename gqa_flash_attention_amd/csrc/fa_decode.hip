@@ -1,12 +1,13 @@
 // Split-KV decode / speculative-verify launcher, the LSE combine kernel and
 // the paged-gather test hook.
 //
-// Split-KV: each workgroup takes one (sequence, KV head, block of rows,
-// chunk of kv_chunk keys) and writes an fp32 partial output normalised by its
-// own row sum plus the row LSE; the combine kernel merges the chunks of a row
-// by their LSE (beellama.cpp PR 149: a combine kernel runs after the split
-// blocks when the KV range is split into parallel blocks, on the same stream,
-// and every partial must publish its (max, rowsum)).
+// Split-KV: a persistent grid, one workgroup per slot the GPU holds at once,
+// streams all K/V tiles in equal contiguous ranges and writes fp32 partial
+// outputs normalised by their own row sums plus the row LSEs, at most two per
+// chunk of kv_chunk keys; the combine kernel merges the partials of a row by
+// their LSE (beellama.cpp PR 149: a combine kernel runs after the split blocks
+// when the KV range is split into parallel blocks, on the same stream, and
+// every partial must publish its (max, rowsum)).
 #include <algorithm>
 
 #include "fa_attn_kernel.h"
@@ -21,14 +22,32 @@ namespace {
 template <int D, int NWR> struct SplitCfg {
   static constexpr int DS = D >= 512 ? 4 : (D >= 256 ? 2 : 1);
   static constexpr int NW = NWR * DS;
-  static constexpr int BN = (NWR == 4 && D <= 128) ? 64 : 32;
+  static constexpr int BN = 32;
   static constexpr int WPE = D <= 128 ? 2 : 1;
-  // tile buffers per operand (measured on MI355X: one row wave streams best
-  // with two, a two-wave block with three; larger head dims are LDS-bound)
-  static constexpr int NBUF = D == 512 ? 2 : (D == 256 ? 3 : ((NWR == 1 || BN * D >= 8192) ? 2 : 3));
-  // several chunks per workgroup
-  static constexpr bool MULTI = true;
+  // tile buffers per operand: two keep 3/4 of the ring in flight; larger
+  // head dims are LDS-bound
+  static constexpr int NBUF = 2;
 };
+
+// Workgroups of a kernel the GPU holds at once: CUs x resident workgroups per
+// CU. Measured on MI355X, a CU holds at most 144 KiB of LDS across
+// workgroups of 32 KiB or less (the occupancy query allows 160), so the
+// count is the smaller of the two.
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, int threads, int (&cache)[16]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (cache[dev] > 0) return cache[dev];
+  int occ = 0, cus = 0;
+  hipFuncAttributes attr{};
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess) occ = 1;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) == hipSuccess &&
+      attr.sharedSizeBytes > 0)
+    occ = std::min<int>(occ, (int)(147456 / attr.sharedSizeBytes));
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+  cache[dev] = std::max(occ, 1) * std::max(cus, 1);
+  return cache[dev];
+}
 
 template <int D, int NWR>
 hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
@@ -53,25 +72,19 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   a.chunk = d.kv_chunk;
-  a.max_chunks = d.max_chunks;
-  // Very large grids of short chunks merge several consecutive chunks into
-  // one workgroup, whose copy stream then runs across chunk boundaries (one
-  // partial per chunk is still written); chunks must be whole tiles for this.
-  // Up to 16384 chunk slots, one chunk per workgroup streams best.
-  const int64_t slots = (int64_t)d.B * d.Hkv * a.n_rb * d.max_chunks;
-  int cpw = 1;
-  if (C::MULTI && d.kv_chunk % C::BN == 0 && slots > 16384)
-    cpw = (int)std::min<int64_t>(d.max_chunks, (slots + 16383) / 16384);
-  a.cpw = cpw;
-  a.n_cg = (d.max_chunks + cpw - 1) / cpw;
-  const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb * a.n_cg;
-  if (grid == 0) return hipSuccess;
+  a.n_slots = d.n_slots;
+  auto kp = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE>;
+  auto kd = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE>;
+  // both kernels reserve the same LDS, so they split the work identically
+  static int cache_p[16], cache_d[16];
+  const int resident = d.table != nullptr ? resident_workgroups(kp, NW * 64, cache_p)
+                                          : resident_workgroups(kd, NW * 64, cache_d);
+  // whole sets of Hkv workgroups, one per KV head
+  const int grid = std::max(resident / d.Hkv, 1) * d.Hkv;
   if (d.table != nullptr)
-    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::MULTI, C::WPE>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL(kp, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::MULTI, C::WPE>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL(kd, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -95,7 +108,7 @@ struct CombineArgs {
   const float* lse_part;
   const int32_t* n_chunks;
   const int32_t* seq_lens;
-  int kv_chunk, max_chunks;
+  int kv_chunk, slots_per_chunk, n_slots;
   uint16_t* o;
   float* lse;
   int B, Sq, Hq;
@@ -113,19 +126,22 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // One wave (one workgroup) per output row (sequence b, query head h, query
-// row i), in two memory round trips: every LSE of the row at once (lane k
-// holds chunks k and k + 64, ...), then every partial slice the lane needs.
-// The lanes cover (chunk, 16-byte slice of D) pairs: with D/4 slices per
-// chunk, CPI = 64 / (D/4) chunks per step (D <= 256), or SPL = (D/4) / 64
-// slices of one chunk per lane (D = 512). A chunk's weight comes from the
-// lane holding its LSE by a lane shuffle.
+// row i). The row's slots are taken in blocks of 256 (four LSEs per lane);
+// the non-empty ones (finite LSE) of a block are listed in LDS by ballot and
+// lane-prefix count, and their partial outputs are fetched CPI x BATCH at a
+// time: with D/4 16-byte slices per partial, the lanes cover (partial, slice)
+// pairs, CPI = 64 / (D/4) partials per step (D <= 256) or SPL = (D/4) / 64
+// slices of one partial per lane (D = 512). Rows of at most 256 slots (the
+// common case) read their LSEs once; longer rows read them once for the max
+// and again per block.
 template <int D>
 __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
-  constexpr int SL = D / 4;                       // float4 slices per chunk
-  constexpr int CPI = SL >= 64 ? 1 : 64 / SL;     // chunks per step
+  constexpr int SL = D / 4;                       // float4 slices per partial
+  constexpr int CPI = SL >= 64 ? 1 : 64 / SL;     // partials per step
   constexpr int SPL = SL >= 64 ? SL / 64 : 1;     // slices per lane
-  constexpr int MAXL = 4;                          // LSEs held per lane: up to 256 chunks at once
-  constexpr int BATCH = 8;                         // partial loads in flight per lane
+  constexpr int BATCH = 16 / SPL;                  // steps whose loads are in flight together
+  __shared__ int s_slot[256];
+  __shared__ float s_lse[256];
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int i = (int)(row % c.Sq);
@@ -133,28 +149,35 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
   const int h = (int)(t % c.Hq);
   const int b = (int)(t / c.Hq);
 
-  int n = c.max_chunks;
+  int n = c.n_slots;
   if (c.n_chunks != nullptr) {
     n = c.n_chunks[b];
   } else if (c.seq_lens != nullptr) {
     const int len = max(c.seq_lens[b], 0);
-    n = (int)(((int64_t)len + c.kv_chunk - 1) / c.kv_chunk);
+    n = (int)((((int64_t)len + c.kv_chunk - 1) / c.kv_chunk) * c.slots_per_chunk);
   }
-  n = max(0, min(n, c.max_chunks));
+  n = max(0, min(n, c.n_slots));
 
-  const float* lp = c.lse_part + row * c.max_chunks;
-  float lv[MAXL];
-  float m = -INFINITY;
+  const float* lp = c.lse_part + row * c.n_slots;
+  const float* op = c.o_part + row * c.n_slots * D;
+  auto load_block = [&](int b0, float (&lv)[4]) {
 #pragma unroll
-  for (int r = 0; r < MAXL; ++r) {
-    const int k = lane + 64 * r;
-    lv[r] = k < n ? lp[k] : -INFINITY;
-    m = fmaxf(m, lv[r]);
+    for (int r = 0; r < 4; ++r) {
+      const int k = b0 + lane + 64 * r;
+      lv[r] = k < n ? lp[k] : -INFINITY;
+    }
+  };
+  float lv[4];
+  load_block(0, lv);
+  float m = fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3]));
+  for (int b0 = 256; b0 < n; b0 += 256) {
+    float lw[4];
+    load_block(b0, lw);
+    m = fmaxf(m, fmaxf(fmaxf(lw[0], lw[1]), fmaxf(lw[2], lw[3])));
   }
-  for (int k = lane + 64 * MAXL; k < n; k += 64) m = fmaxf(m, lp[k]);   // rows with > 256 chunks
   m = wave_max(m);
 
-  const int co = CPI > 1 ? lane / SL : 0;         // chunk offset of this lane in a step
+  const int co = CPI > 1 ? lane / SL : 0;         // partial offset of this lane in a step
   const int sl = CPI > 1 ? lane % SL : lane;      // first slice of this lane
   f32x4 acc[SPL];
 #pragma unroll
@@ -162,41 +185,50 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
   float lse_out = -INFINITY;
   if (m != -INFINITY) {
     float tot = 0.f;
+    for (int b0 = 0; b0 < n; b0 += 256) {
+      if (b0 > 0) load_block(b0, lv);
+      // list the block's non-empty slots (empty ones: weight 0, O never read)
+      int nv = 0;
 #pragma unroll
-    for (int r = 0; r < MAXL; ++r) tot += fast_exp2((lv[r] - m) * kLog2e);
-    for (int k = lane + 64 * MAXL; k < n; k += 64) tot += fast_exp2((lp[k] - m) * kLog2e);
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = lv[r] != -INFINITY;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(ok);
+        const int pos = nv + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (ok) {
+          s_slot[pos] = b0 + lane + 64 * r;
+          s_lse[pos] = lv[r];
+          tot += fast_exp2((lv[r] - m) * kLog2e);
+        }
+        nv += __builtin_popcountll(mask);
+      }
+      __syncthreads();
+      for (int k0 = 0; k0 < nv; k0 += CPI * BATCH) {
+        f32x4 x[BATCH][SPL];
+        float e[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int j = k0 + CPI * u + co;
+          const bool ok = j < nv;
+          const int slot = ok ? s_slot[j] : 0;
+          e[u] = ok ? fast_exp2((s_lse[j] - m) * kLog2e) : 0.f;
+#pragma unroll
+          for (int v = 0; v < SPL; ++v)
+            x[u][v] = ok ? *reinterpret_cast<const f32x4*>(op + (int64_t)slot * D + 4 * (sl + 64 * v))
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+          for (int v = 0; v < SPL; ++v) acc[v] += e[u] * x[u][v];
+      }
+      __syncthreads();                            // the list is rewritten by the next block
+    }
     tot = wave_sum(tot);
     const float inv = 1.0f / tot;
     lse_out = m + fast_log2(tot) * kLn2;
-    const float* op = c.o_part + row * c.max_chunks * D;
-    for (int k0 = 0; k0 < n; k0 += CPI * BATCH) {
-      f32x4 x[BATCH][SPL];
-      float lk[BATCH];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int k = k0 + CPI * u + co;
-        // the LSE of chunk k sits in lane k % 64, register k / 64 (< 256 chunks)
-        // (k / 64 is the same for the whole wave: 64 is a multiple of CPI)
-        float src = lv[0];
-#pragma unroll
-        for (int r = 1; r < MAXL; ++r)
-          if (((k0 + CPI * u) >> 6) == r) src = lv[r];
-        const float from_lane = __shfl(src, k & 63, 64);
-        lk[u] = k < n ? (k < 64 * MAXL ? from_lane : lp[k]) : -INFINITY;
-#pragma unroll
-        for (int v = 0; v < SPL; ++v)
-          x[u][v] = (k < n && lk[u] != -INFINITY)
-                        ? *reinterpret_cast<const f32x4*>(op + (int64_t)k * D + 4 * (sl + 64 * v))
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        // empty chunk (LSE -inf): weight 0 and its contents are never read
-        const float w = lk[u] == -INFINITY ? 0.f : fast_exp2((lk[u] - m) * kLog2e) * inv;
-#pragma unroll
-        for (int v = 0; v < SPL; ++v) acc[v] += w * x[u][v];
-      }
-    }
+    for (int v = 0; v < SPL; ++v) acc[v] *= inv;
     // add the CPI lane groups that hold the same slice
 #pragma unroll
     for (int sft = 32; sft >= SL && CPI > 1; sft >>= 1)
@@ -218,7 +250,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
 
 template <int D>
 hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
-  CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.max_chunks,
+  CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.slots_per_chunk, d.n_slots,
                 static_cast<uint16_t*>(d.o), d.lse, d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
   if (rows == 0) return hipSuccess;

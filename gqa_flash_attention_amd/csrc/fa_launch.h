@@ -6,6 +6,10 @@
 
 namespace gqafa {
 
+// Split-KV partial slots per chunk of kv_chunk keys: the balanced split cuts
+// a chunk between at most this many workgroups, each leaving one partial.
+constexpr int kSlotsPerChunk = 4;
+
 struct PrefillDesc {
   const void* q; const void* k; const void* v; void* o; float* lse;
   int B, Hq, Hkv, Sq, Skv, D, causal, window;
@@ -15,16 +19,16 @@ struct PrefillDesc {
 struct SplitDesc {
   const void* q; const void* kcache; const void* vcache;
   const int32_t* table; const int32_t* seq_lens;
-  float* o_part; float* lse_part;
-  int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, max_chunks, causal, window;
+  float* o_part; float* lse_part;   // [B, Hq, Sq, n_slots(, D)]: kSlotsPerChunk per chunk
+  int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, n_slots, causal, window;
   float scale;
 };
 
 struct CombineDesc {
   const float* o_part; const float* lse_part;
-  const int32_t* n_chunks;   // device [B] or null
-  const int32_t* seq_lens;   // used when n_chunks is null and kv_chunk > 0
-  int kv_chunk, max_chunks;
+  const int32_t* n_chunks;   // device [B] or null: partials to merge per sequence
+  const int32_t* seq_lens;   // used when n_chunks is null: slots_per_chunk * ceil(len / kv_chunk)
+  int kv_chunk, slots_per_chunk, n_slots;   // n_slots: slots per row in memory
   void* o; float* lse;
   int B, Sq, Hq, D;
 };

@@ -33,7 +33,7 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   a.n_rb = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, false, C::WPE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE>), dim3((unsigned)grid),
                      dim3(C::NW * 64), 0, stream, a);
   return hipGetLastError();
 }

@@ -69,16 +69,20 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
- * [B, Hq, Sq, n_chunks, D] and their LSEs [B, Hq, Sq, n_chunks], with
- * n_chunks = ceil(max_seq_len / kv_chunk), each region 256-byte aligned.
- * Returns 0 for invalid sizes.
+ * [B, Hq, Sq, n_slots, D] and their LSEs [B, Hq, Sq, n_slots], with
+ * n_slots = 4 * ceil(max_seq_len / kv_chunk) (the balanced split cuts a
+ * chunk between at most four workgroups, each leaving one partial), each
+ * region 256-byte aligned. Returns 0 for invalid sizes.
  */
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk);
 
 /*
  * Decode (Sq = 1) and speculative verify (a few query rows, causal among
  * them) over a paged KV cache, split over the KV sequence in chunks of
- * kv_chunk tokens and merged by LSE (split-KV, "parallel blocks" + combine).
+ * kv_chunk tokens and merged by LSE (split-KV, "parallel blocks" + combine:
+ * beellama.cpp PR 149, Overview). The split kernel is a persistent grid that
+ * gives every workgroup an equal share of all K/V tiles; each partial covers
+ * all or part of one chunk.
  *
  *   q           bf16 [B, Sq, Hq, D]: the Sq newest rows of each sequence
  *   kcache      bf16 [num_pages, page_size, Hkv, D] when block_table != NULL;
@@ -100,13 +104,18 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
  *               unspecified. Entries past a sequence's last page are never
  *               used.
  *   page_size   a power of two in [1, 65536]
- *   kv_chunk    tokens per split, > 0
+ *   kv_chunk    tokens per chunk, > 0 (a multiple of 32 keeps every tile whole)
  *   workspace   device buffer of at least
  *               fa_decode_workspace_bytes(B, Sq, Hq, D, max_pages_per_seq*page_size, kv_chunk)
  *
  * Two kernels run on `stream`: the split kernel writes partials into the
  * workspace, then the combine kernel writes o and lse. Calls that share a
- * workspace must be ordered on one stream.
+ * workspace must be ordered on one stream. Results are deterministic: the
+ * work split depends only on the shapes, seq_lens and the GPU's size.
+ * Returns FA_ERR_INVALID_ARG when the K/V tile count of one call does not
+ * fit 32 bits (B * Hkv * ceil(Sq * Hq / Hkv / 32) * (ceil(max_len / 32) +
+ * ceil(max_len / kv_chunk)) > 2^31 - 1, max_len = max_pages_per_seq *
+ * page_size).
  */
 int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
                     const int32_t* block_table, const int32_t* seq_lens,
