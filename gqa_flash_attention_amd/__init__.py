@@ -7,6 +7,7 @@ runs in the HIP kernels; nothing here falls back to another implementation.
 
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -14,7 +15,7 @@ import torch
 from ._lib import FAError, check, load  # noqa: F401
 
 __all__ = ["prefill", "decode_paged", "decode_workspace_bytes", "combine_lse",
-           "paged_gather", "FAError", "load"]
+           "kv_append", "paged_gather", "FAError", "load"]
 
 
 def _ptr(t):
@@ -25,36 +26,52 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require(t, name, dtype, device=None):
+def _require(t, name, dtype, device=None, strided=False):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be 4-D with a unit-stride last dimension")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _strides(t):
+    """(outer, token, head) element strides of a 4-D view, as a C int64[3]."""
+    return (ctypes.c_int64 * 3)(*t.stride()[:3])
+
+
 def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | None = None,
             out=None, lse=None, return_lse: bool = True):
-    """q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16 -> (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32)."""
+    """q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16 -> (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32).
+
+    q, k, v and out may be strided views (e.g. slices of one fused QKV
+    tensor); only their last dimension must be unit-stride.
+    """
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n, torch.bfloat16, dev)
+        _require(t, n, torch.bfloat16, dev, strided=True)
     if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("shape mismatch between q, k and v")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev, strided=True)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    check(load().fa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                            B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), int(window), float(scale),
-                            _stream(dev)))
+    check(load().fa_prefill_strided(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                    _ptr(out), _strides(out), _ptr(lse),
+                                    B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), int(window),
+                                    float(scale), _stream(dev)))
     return out, lse
 
 
@@ -71,12 +88,14 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
     q [B,Sq,Hq,D] bf16; with block_table (int32 [B, max_pages]) the caches are
     [num_pages, page_size, Hkv, D]; without it they are contiguous
     [B, Smax, Hkv, D] (Smax a multiple of page_size). seq_lens int32 [B].
+    q, the caches and out may be strided views with a unit-stride last
+    dimension (e.g. K and V interleaved in one allocation).
     """
     B, Sq, Hq, D = q.shape
     dev = q.device
-    _require(q, "q", torch.bfloat16, dev)
-    _require(kcache, "kcache", torch.bfloat16, dev)
-    _require(vcache, "vcache", torch.bfloat16, dev)
+    _require(q, "q", torch.bfloat16, dev, strided=True)
+    _require(kcache, "kcache", torch.bfloat16, dev, strided=True)
+    _require(vcache, "vcache", torch.bfloat16, dev, strided=True)
     _require(seq_lens, "seq_lens", torch.int32, dev)
     if vcache.shape != kcache.shape:
         raise ValueError("kcache and vcache differ in shape")
@@ -98,14 +117,18 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev, strided=True)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    check(load().fa_decode_paged(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
-                                 _ptr(seq_lens), _ptr(out), _ptr(lse),
-                                 B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
-                                 int(bool(causal)), int(window), float(scale),
-                                 _ptr(workspace), workspace.numel(), _stream(dev)))
+    check(load().fa_decode_paged_strided(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
+                                         _ptr(vcache), _strides(vcache), _ptr(block_table),
+                                         _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
+                                         B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
+                                         int(bool(causal)), int(window), float(scale),
+                                         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, lse
 
 
@@ -124,6 +147,36 @@ def combine_lse(o_part, lse_part, n_chunks=None, *, out=None, lse=None):
     check(load().fa_combine_lse(_ptr(o_part), _ptr(lse_part), _ptr(n_chunks), C, _ptr(out),
                                 _ptr(lse), B, Sq, Hq, D, _stream(dev)))
     return out, lse
+
+
+def kv_append(kcache, vcache, block_table, seq_lens, knew, vnew, *, page_size: int = 16):
+    """Write knew/vnew [B, Snew, Hkv, D] into the caches in place.
+
+    Row i of sequence b goes to token seq_lens[b] - Snew + i (seq_lens counts
+    the new rows). With block_table the caches are [num_pages, page_size,
+    Hkv, D], else contiguous [B, Smax, Hkv, D]. Every tensor may be a strided
+    view with a unit-stride last dimension.
+    """
+    B, Snew, Hkv, D = knew.shape
+    dev = knew.device
+    for t, n in ((kcache, "kcache"), (vcache, "vcache"), (knew, "knew"), (vnew, "vnew")):
+        _require(t, n, torch.bfloat16, dev, strided=True)
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    if vnew.shape != knew.shape or vcache.shape != kcache.shape or kcache.shape[2:] != (Hkv, D):
+        raise ValueError("shape mismatch between caches and new rows")
+    if block_table is not None:
+        _require(block_table, "block_table", torch.int32, dev)
+        if kcache.shape[1] != page_size:
+            raise ValueError("cache page dimension differs from page_size")
+        num_pages, max_pages = kcache.shape[0], block_table.shape[1]
+    else:
+        if kcache.shape[1] % page_size:
+            raise ValueError("contiguous cache length must be a multiple of page_size")
+        num_pages, max_pages = 0, kcache.shape[1] // page_size
+    check(load().fa_kv_append(_ptr(kcache), _strides(kcache), _ptr(vcache), _strides(vcache),
+                              _ptr(block_table), _ptr(seq_lens), _ptr(knew), _strides(knew),
+                              _ptr(vnew), _strides(vnew), B, Snew, Hkv, D, num_pages, page_size,
+                              max_pages, _stream(dev)))
 
 
 def paged_gather(cache, block_table, seq_lens, *, out=None):

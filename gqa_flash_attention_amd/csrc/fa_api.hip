@@ -33,6 +33,21 @@ int to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 // this keeps the 1-D grids below 2^31 workgroups).
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
+// Element strides (outer, token, head) from a caller's host array, or the
+// dense layout when it is NULL. Every stride is a non-negative multiple of 8
+// elements (each row stays 16-byte aligned) below 2^40; a K/V token stride is
+// below 2^24 (the kernels keep a tile's per-lane offsets in 32 bits).
+bool get_strides(const int64_t* st, Strides dense, bool kv, Strides& out) {
+  if (st == nullptr) {
+    out = dense;
+    return true;
+  }
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0 || st[i] >= (int64_t(1) << 40)) return false;
+  out = Strides{st[0], st[1], st[2]};
+  return !(kv && out.token >= (int64_t(1) << 24));
+}
+
 }  // namespace
 
 extern "C" {
@@ -48,22 +63,36 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
-               int B, int Hq, int Hkv, int Sq, int Skv, int D,
-               int causal, int window, float scale, void* stream) {
+int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
+                       const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
+                       float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                       int causal, int window, float scale, void* stream) {
   if (B < 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  Strides qs, ks, vs, os;
+  const Strides qd{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
+  const Strides kd{(int64_t)Skv * Hkv * D, (int64_t)Hkv * D, D};
+  if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, qd, false, os) ||
+      !get_strides(k_stride, kd, true, ks) || !get_strides(v_stride, kd, true, vs))
+    return FA_ERR_INVALID_ARG;
   if (B == 0 || Sq == 0) return FA_OK;
   if (!q || !o || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (Skv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   if ((int64_t)B * Hkv * ((rows + 127) / 32) > kMaxGrid) return FA_ERR_INVALID_ARG;
-  PrefillDesc d{q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, window, scale};
+  PrefillDesc d{q, k, v, o, lse, qs, ks, vs, os, B, Hq, Hkv, Sq, Skv, D, causal, window, scale};
   return to_status(launch_prefill(d, static_cast<hipStream_t>(stream)));
+}
+
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Sq, int Skv, int D,
+               int causal, int window, float scale, void* stream) {
+  return fa_prefill_strided(q, nullptr, k, nullptr, v, nullptr, o, nullptr, lse, B, Hq, Hkv, Sq, Skv, D,
+                            causal, window, scale, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
@@ -75,13 +104,15 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
   return o_bytes + l_bytes;
 }
 
-int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
-                    const int32_t* block_table, const int32_t* seq_lens,
-                    void* o, float* lse,
-                    int B, int Sq, int Hq, int Hkv, int D,
-                    int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
-                    int causal, int window, float scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
+                            const void* kcache, const int64_t* k_stride,
+                            const void* vcache, const int64_t* v_stride,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            void* o, const int64_t* o_stride, float* lse,
+                            int B, int Sq, int Hq, int Hkv, int D,
+                            int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                            int causal, int window, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (max_pages_per_seq < 0 || kv_chunk <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -93,6 +124,13 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
   const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
   if (max_len > INT32_MAX) return FA_ERR_INVALID_ARG;
   if (block_table != nullptr && num_pages <= 0) return FA_ERR_INVALID_ARG;
+  Strides qs, ks, vs, os;
+  const Strides qd{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
+  const Strides kd = block_table != nullptr ? Strides{(int64_t)page_size * Hkv * D, (int64_t)Hkv * D, D}
+                                            : Strides{max_len * Hkv * D, (int64_t)Hkv * D, D};
+  if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, qd, false, os) ||
+      !get_strides(k_stride, kd, true, ks) || !get_strides(v_stride, kd, true, vs))
+    return FA_ERR_INVALID_ARG;
   if (B == 0 || Sq == 0) return FA_OK;
   if (!q || !o || !seq_lens || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (max_len > 0 && (!kcache || !vcache || !aligned16(kcache) || !aligned16(vcache)))
@@ -116,15 +154,28 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
                                              align256((size_t)(prow * n_slots * D) * sizeof(float)));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (max_chunks > 0) {
-    SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part,
+    SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part, qs, ks, vs,
                  B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
                  (int)n_slots, causal, window, scale};
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
   CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)kSlotsPerChunk, (int)n_slots,
-                 o, lse, B, Sq, Hq, D};
+                 o, lse, os, B, Sq, Hq, D};
   return to_status(launch_combine(cd, st));
+}
+
+int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* o, float* lse,
+                    int B, int Sq, int Hq, int Hkv, int D,
+                    int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                    int causal, int window, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_decode_paged_strided(q, nullptr, kcache, nullptr, vcache, nullptr, block_table, seq_lens,
+                                 o, nullptr, lse, B, Sq, Hq, Hkv, D, num_pages, page_size,
+                                 max_pages_per_seq, kv_chunk, causal, window, scale, workspace,
+                                 workspace_bytes, stream);
 }
 
 int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_chunks,
@@ -137,8 +188,37 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
   if (max_chunks > 0 && (!o_part || !lse_part || !aligned16(o_part))) return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
-  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, 1, max_chunks, o, lse, B, Sq, Hq, D};
+  const Strides od{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, 1, max_chunks, o, lse, od, B, Sq, Hq, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
+}
+
+int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int64_t* v_stride,
+                 const int32_t* block_table, const int32_t* seq_lens,
+                 const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
+                 int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
+                 void* stream) {
+  if (B < 0 || Snew < 0 || Hkv <= 0 || max_pages_per_seq < 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  const int page_shift = log2_exact(page_size);
+  if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
+  const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
+  if (max_len > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (block_table != nullptr && num_pages <= 0) return FA_ERR_INVALID_ARG;
+  Strides kcs, vcs, kns, vns;
+  const Strides cd = block_table != nullptr ? Strides{(int64_t)page_size * Hkv * D, (int64_t)Hkv * D, D}
+                                            : Strides{max_len * Hkv * D, (int64_t)Hkv * D, D};
+  const Strides nd{(int64_t)Snew * Hkv * D, (int64_t)Hkv * D, D};
+  if (!get_strides(k_stride, cd, false, kcs) || !get_strides(v_stride, cd, false, vcs) ||
+      !get_strides(knew_stride, nd, false, kns) || !get_strides(vnew_stride, nd, false, vns))
+    return FA_ERR_INVALID_ARG;
+  if (B == 0 || Snew == 0 || max_len == 0) return FA_OK;
+  if (!kcache || !vcache || !knew || !vnew || !seq_lens) return FA_ERR_INVALID_ARG;
+  if (!aligned16(kcache) || !aligned16(vcache) || !aligned16(knew) || !aligned16(vnew))
+    return FA_ERR_INVALID_ARG;
+  AppendDesc d{kcache, vcache, knew, vnew, block_table, seq_lens, kcs, vcs, kns, vns,
+               B, Snew, Hkv, D, num_pages, page_shift, max_pages_per_seq};
+  return to_status(launch_append(d, static_cast<hipStream_t>(stream)));
 }
 
 int fa_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,

@@ -71,7 +71,13 @@ struct AttnArgs {
   const int32_t* seq_lens;  // split mode: keys per sequence
   const int32_t* table;     // split mode: block table or null
   int page_shift, max_pages, num_pages;
-  int64_t slots;          // contiguous layout: token slots per sequence
+  // element strides; the head dim is unit-stride. K/V: (sequence, token,
+  // head) for a dense cache, (page, slot, head) for a paged one. The token
+  // strides of K and V are below 2^24 (checked by the caller).
+  int64_t q_sb, q_ss, q_sh;
+  int64_t o_sb, o_ss, o_sh;   // prefill output
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
   int B, Sq, Hq, Hkv, G;
   int skv;                // prefill: keys per sequence
   int causal, window;
@@ -210,7 +216,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // Segment s (1 KiB) of a tile holds chunk positions 64 s .. 64 s + 63 of
   // the row-major tile: lane L writes position 64 s + L = row * KCH + pc,
   // holding logical chunk pc ^ swizzle(row) of that key row.
-  const int64_t row_stride = (int64_t)a.Hkv * D;
+  const int k_rs = (int)a.k_ss, v_rs = (int)a.v_ss;   // token strides (elements)
   // Per-lane segment geometry. With few segments per wave it is kept in
   // registers; with many (large head dims, few waves) it is recomputed at
   // each copy, which costs a few integer operations instead of 3 registers
@@ -220,11 +226,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   auto seg_row = [&](int i) -> int { return ((wave * SEGW + i) * 64 + lane) / KCH; };
   auto seg_koff = [&](int i) -> uint32_t {
     const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
-    return 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_k<D>(row)));
+    return 2u * (uint32_t)(row * k_rs + 8 * (pc ^ swz_k<D>(row)));
   };
   auto seg_voff = [&](int i) -> uint32_t {
     const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
-    return 2u * (uint32_t)(row * (int)row_stride + 8 * (pc ^ swz_v<D>(row)));
+    return 2u * (uint32_t)(row * v_rs + 8 * (pc ^ swz_v<D>(row)));
   };
   int srow[NKEEP];         // key row (inside the tile) of each of this lane's segments
   uint32_t koff[NKEEP];    // byte offset of its K chunk inside an unclamped tile
@@ -264,6 +270,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   auto issue = [&](int tb, int ke_t, const uint16_t* kv_base, int b_t, bool is_v, uint16_t* dst) {
     const int lim = ke_t - 1 - tb;            // last valid row of this tile
     const bool tail = lim < BN - 1;           // uniform
+    const int rs = is_v ? v_rs : k_rs;
     if constexpr (PAGED && TAB > 0) {
       const int pf = tb >> a.page_shift, pl = (tb + min(lim, BN - 1)) >> a.page_shift;
       if (b_t != tw_b || pf < tw_p0 || pl >= tw_p0 + TAB) stage_table(b_t, pf);
@@ -282,24 +289,27 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           page = a.table[(int64_t)b_t * a.max_pages + (t >> a.page_shift)];
           page = min(max(page, 0), a.num_pages - 1);
         }
-        const int64_t base = ((((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1))) -
-                              row) * row_stride;
+        const int64_t base = (int64_t)page * (is_v ? a.v_sb : a.k_sb) +
+                             (int64_t)((t & ((1 << a.page_shift) - 1)) - row) * rs;
         src = reinterpret_cast<const char*>(kv_base + base) + off0;
       } else {
         // uniform tile base + 32-bit per-lane byte offset
         uint32_t o = off0;
-        if (tail && row > lim) o -= 2u * (uint32_t)((row - lim) * (int)row_stride);
-        src = reinterpret_cast<const char*>(kv_base + (int64_t)tb * row_stride) + o;
+        if (tail && row > lim) o -= 2u * (uint32_t)((row - lim) * rs);
+        src = reinterpret_cast<const char*>(kv_base + (int64_t)tb * rs) + o;
       }
       dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
     }
   };
   // K and V cache bases of (sequence b, KV head g)
   auto kv_bases = [&](int b_t, int g_t, const uint16_t*& kb_out, const uint16_t*& vb_out) {
-    int64_t off = (int64_t)g_t * D;
-    if constexpr (!PAGED) off += (int64_t)b_t * a.slots * row_stride;
-    kb_out = a.k + off;
-    vb_out = a.v + off;
+    int64_t koff = (int64_t)g_t * a.k_sh, voff = (int64_t)g_t * a.v_sh;
+    if constexpr (!PAGED) {
+      koff += (int64_t)b_t * a.k_sb;
+      voff += (int64_t)b_t * a.v_sb;
+    }
+    kb_out = a.k + koff;
+    vb_out = a.v + voff;
   };
 
   // ---- the rows being worked on: one block of rows of one (b, KV head) ------
@@ -324,7 +334,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     qi = row_ok ? r / a.G : 0;
     qh = g_ * a.G + (row_ok ? r % a.G : 0);
     p = qi + shift;                            // absolute position of this lane's row
-    const int64_t qoff = (((int64_t)b_ * a.Sq + qi) * a.Hq + qh) * D + 8 * hl + dh * (D / DS);
+    const int64_t qoff = (int64_t)b_ * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)qh * a.q_sh +
+                         8 * hl + dh * (D / DS);
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
@@ -875,7 +886,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : fast_rcp(l_tot);
     const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
-    uint16_t* dst = a.o + (((int64_t)b * a.Sq + qi) * a.Hq + qh) * D;
+    uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)qh * a.o_sh;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -65,7 +65,9 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   a.page_shift = d.page_shift;
   a.max_pages = d.max_pages;
   a.num_pages = d.num_pages;
-  a.slots = (int64_t)d.max_pages << d.page_shift;
+  a.q_sb = d.qs.outer; a.q_ss = d.qs.token; a.q_sh = d.qs.head;
+  a.k_sb = d.ks.outer; a.k_ss = d.ks.token; a.k_sh = d.ks.head;
+  a.v_sb = d.vs.outer; a.v_ss = d.vs.token; a.v_sh = d.vs.head;
   a.B = d.B; a.Sq = d.Sq; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.Hq / d.Hkv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
@@ -111,6 +113,7 @@ struct CombineArgs {
   int kv_chunk, slots_per_chunk, n_slots;
   uint16_t* o;
   float* lse;
+  int64_t o_sb, o_ss, o_sh;     // element strides of o (sequence, row, head)
   int B, Sq, Hq;
 };
 
@@ -238,7 +241,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
         for (int e = 0; e < 4; ++e) acc[v][e] += __shfl_xor(acc[v][e], sft, 64);
   }
   if (co == 0) {
-    uint16_t* dst = c.o + (((int64_t)b * c.Sq + i) * c.Hq + h) * D;
+    uint16_t* dst = c.o + (int64_t)b * c.o_sb + (int64_t)i * c.o_ss + (int64_t)h * c.o_sh;
 #pragma unroll
     for (int v = 0; v < SPL; ++v) {
       u32x2 val = {pack_bf16(acc[v][0], acc[v][1]), pack_bf16(acc[v][2], acc[v][3])};
@@ -251,7 +254,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
 template <int D>
 hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
   CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.slots_per_chunk, d.n_slots,
-                static_cast<uint16_t*>(d.o), d.lse, d.B, d.Sq, d.Hq};
+                static_cast<uint16_t*>(d.o), d.lse, d.os.outer, d.os.token, d.os.head, d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0, stream, c);

@@ -10,8 +10,15 @@ namespace gqafa {
 // a chunk between at most this many workgroups, each leaving one partial.
 constexpr int kSlotsPerChunk = 4;
 
+// Element strides of a [B, S, H, D] tensor (or a paged cache [pages, slots,
+// H, D]): outer (batch or page), token (or slot), head; D is unit-stride.
+struct Strides {
+  int64_t outer, token, head;
+};
+
 struct PrefillDesc {
   const void* q; const void* k; const void* v; void* o; float* lse;
+  Strides qs, ks, vs, os;
   int B, Hq, Hkv, Sq, Skv, D, causal, window;
   float scale;
 };
@@ -20,6 +27,7 @@ struct SplitDesc {
   const void* q; const void* kcache; const void* vcache;
   const int32_t* table; const int32_t* seq_lens;
   float* o_part; float* lse_part;   // [B, Hq, Sq, n_slots(, D)]: kSlotsPerChunk per chunk
+  Strides qs, ks, vs;
   int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, n_slots, causal, window;
   float scale;
 };
@@ -30,7 +38,15 @@ struct CombineDesc {
   const int32_t* seq_lens;   // used when n_chunks is null: slots_per_chunk * ceil(len / kv_chunk)
   int kv_chunk, slots_per_chunk, n_slots;   // n_slots: slots per row in memory
   void* o; float* lse;
+  Strides os;                // o [B, Sq, Hq, D]
   int B, Sq, Hq, D;
+};
+
+struct AppendDesc {
+  void* kcache; void* vcache; const void* knew; const void* vnew;
+  const int32_t* table; const int32_t* seq_lens;
+  Strides kcs, vcs, kns, vns;
+  int B, Snew, Hkv, D, num_pages, page_shift, max_pages;
 };
 
 struct GatherDesc {
@@ -43,5 +59,6 @@ hipError_t launch_prefill(const PrefillDesc& d, hipStream_t stream);
 hipError_t launch_split(const SplitDesc& d, hipStream_t stream);
 hipError_t launch_combine(const CombineDesc& d, hipStream_t stream);
 hipError_t launch_gather(const GatherDesc& d, hipStream_t stream);
+hipError_t launch_append(const AppendDesc& d, hipStream_t stream);
 
 }  // namespace gqafa

@@ -27,7 +27,10 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   a.v = static_cast<const uint16_t*>(d.v);
   a.o = static_cast<uint16_t*>(d.o);
   a.lse = d.lse;
-  a.slots = d.Skv;
+  a.q_sb = d.qs.outer; a.q_ss = d.qs.token; a.q_sh = d.qs.head;
+  a.o_sb = d.os.outer; a.o_ss = d.os.token; a.o_sh = d.os.head;
+  a.k_sb = d.ks.outer; a.k_ss = d.ks.token; a.k_sh = d.ks.head;
+  a.v_sb = d.vs.outer; a.v_ss = d.vs.token; a.v_sh = d.vs.head;
   a.B = d.B; a.Sq = d.Sq; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.Hq / d.Hkv;
   a.skv = d.Skv;
   a.causal = d.causal; a.window = d.window;

@@ -68,6 +68,27 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                int causal, int window, float scale, void* stream);
 
 /*
+ * fa_prefill on strided views, so that callers need not copy slices (for
+ * example q, k and v cut from one fused QKV projection) into contiguous
+ * tensors first. Inputs are read and the output written by stride (ATOM
+ * PR 2938, Summary: the kernel reads by token and block strides and only the
+ * innermost dimension must be unit-stride).
+ *
+ *   q_stride, k_stride, v_stride, o_stride: host arrays of three int64
+ *   element strides (batch, token, head) of the [B, S, H, D] tensors; the
+ *   head dim D is unit-stride. NULL means the contiguous layout. Each stride
+ *   is a non-negative multiple of 8 below 2^40 (every row 16-byte aligned);
+ *   the token strides of k and v are below 2^24. o must not overlap itself
+ *   or the inputs. Returns FA_ERR_INVALID_ARG otherwise; the rest is as
+ *   fa_prefill, and the results are bitwise those of fa_prefill on
+ *   contiguous copies of the same values.
+ */
+int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
+                       const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
+                       float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                       int causal, int window, float scale, void* stream);
+
+/*
  * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
  * [B, Hq, Sq, n_slots, D] and their LSEs [B, Hq, Sq, n_slots], with
  * n_slots = 4 * ceil(max_seq_len / kv_chunk) (the balanced split cuts a
@@ -126,6 +147,26 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_paged on strided views (ATOM PR 2938, Summary: read by stride,
+ * only the innermost dimension unit-stride). q_stride and o_stride are the
+ * (batch, row, head) element strides of q and o; k_stride and v_stride the
+ * (page, slot, head) strides of a paged cache, or (sequence, token, head) of
+ * a contiguous one, so K and V may for example be interleaved in one
+ * allocation. Each is a host array of three int64, NULL for the contiguous
+ * layout, with the rules of fa_prefill_strided. The results are bitwise
+ * those of fa_decode_paged on contiguous copies of the same values.
+ */
+int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
+                            const void* kcache, const int64_t* k_stride,
+                            const void* vcache, const int64_t* v_stride,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            void* o, const int64_t* o_stride, float* lse,
+                            int B, int Sq, int Hq, int Hkv, int D,
+                            int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                            int causal, int window, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Merge split-KV partials by their LSE:
  *   M = max_c LSE_c,  LSE = M + ln sum_c exp(LSE_c - M),
  *   O = sum_c exp(LSE_c - LSE) * O_c.
@@ -142,6 +183,34 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
 int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_chunks,
                    int max_chunks, void* o, float* lse,
                    int B, int Sq, int Hq, int D, void* stream);
+
+/*
+ * KV-cache append: the step before a decode or verify call, which writes the
+ * Snew newest K/V rows of each sequence into the cache.
+ *
+ *   kcache, vcache  bf16 [num_pages, page_size, Hkv, D] with block_table
+ *                   (int32 [B, max_pages_per_seq]), or contiguous
+ *                   [B, max_pages_per_seq * page_size, Hkv, D] when
+ *                   block_table is NULL; written in place
+ *   seq_lens        int32 [B] on the device: tokens in each cache AFTER the
+ *                   append (the convention of fa_decode_paged); clamped to
+ *                   [0, max_pages_per_seq * page_size]
+ *   knew, vnew      bf16 [B, Snew, Hkv, D]: row i of sequence b goes to token
+ *                   seq_lens[b] - Snew + i
+ *   *_stride        host int64[3] element strides (outer, token, head) of the
+ *                   four tensors, NULL for the contiguous layout, with the
+ *                   rules of fa_prefill_strided (head dim unit-stride)
+ *
+ * Rows whose token would be negative (a sequence shorter than Snew) and rows
+ * whose block-table entry is outside [0, num_pages) are not written. Two new
+ * rows mapped to the same physical slot race (a caller error). The copy is
+ * bit-exact.
+ */
+int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int64_t* v_stride,
+                 const int32_t* block_table, const int32_t* seq_lens,
+                 const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
+                 int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
+                 void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_ref,
     combine_ref,
     decode_paged_ref,
+    kv_append_ref,
     paged_gather_ref,
     partial_attention_ref,
     to_f64,

@@ -52,6 +52,7 @@ __all__ = [
     "decode_paged_ref",
     "partial_attention_ref",
     "combine_ref",
+    "kv_append_ref",
 ]
 
 
@@ -274,3 +275,49 @@ def combine_ref(o_part, lse_part, n_chunks=None):
         o[b] = np.transpose(ob, (1, 0, 2))
         lse[b] = L
     return o, lse
+
+
+def kv_append_ref(kcache, vcache, block_table, seq_lens, knew, vnew, *, page_size: int,
+                  num_pages: int | None = None):
+    """Write the Snew newest K/V rows of each sequence into copies of the caches.
+
+    A pure index map, the step before a decode call over the same cache.
+    seq_lens counts the tokens in each cache after the append (the decode
+    convention), so new row i of sequence b lands at token
+    t = len_b - Snew + i, with len_b clamped to [0, pages_per_seq *
+    page_size]. With block_table [B, pages_per_seq] the caches are
+    [num_pages, page_size, Hkv, D] and token t lives at page
+    block_table[b, t // page_size], slot t % page_size; with block_table None
+    they are [B, Smax, Hkv, D]. Rows with t < 0, and rows whose page is
+    outside [0, num_pages), are not written (readings of this build: the
+    pages do not describe the append). Returns (kcache', vcache').
+    """
+    def copy(x):
+        return x.clone() if hasattr(x, "clone") else np.array(x, copy=True)
+
+    kc, vc = copy(kcache), copy(vcache)
+    lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    B, snew = knew.shape[0], knew.shape[1]
+    if block_table is None:
+        cap = kc.shape[1]
+    else:
+        bt = np.asarray(block_table, dtype=np.int64)
+        cap = bt.shape[1] * page_size
+        if num_pages is None:
+            num_pages = kc.shape[0]
+    for b in range(B):
+        n = min(max(int(lens[b]), 0), cap)
+        for i in range(snew):
+            t = n - snew + i
+            if t < 0:
+                continue
+            if block_table is None:
+                kc[b, t] = knew[b, i]
+                vc[b, t] = vnew[b, i]
+            else:
+                page = int(bt[b, t // page_size])
+                if page < 0 or page >= num_pages:
+                    continue
+                kc[page, t % page_size] = knew[b, i]
+                vc[page, t % page_size] = vnew[b, i]
+    return kc, vc

@@ -32,8 +32,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == sorted(["fa_prefill", "fa_decode_workspace_bytes", "fa_decode_paged",
-                            "fa_combine_lse", "fa_status_string", "fa_paged_gather"])
+    assert names == sorted(["fa_prefill", "fa_prefill_strided", "fa_decode_workspace_bytes",
+                            "fa_decode_paged", "fa_decode_paged_strided", "fa_combine_lse",
+                            "fa_kv_append", "fa_status_string", "fa_paged_gather"])
     assert set(names) == set(_lib.SIGNATURES)
 
 
@@ -140,3 +141,45 @@ def test_gather_validation(lib, kw, want):
     st = lib.fa_paged_gather(a["cache"], a["table"], a["lens"], a["out"], a["B"], a["Hkv"], a["D"],
                              a["num_pages"], a["page_size"], a["max_pages"], None)
     assert st == want
+
+
+def _st(a, b, c):
+    return (ctypes.c_int64 * 3)(a, b, c)
+
+
+def test_strided_prefill_validation(lib):
+    f = lib.fa_prefill_strided
+    def call(qs=None, ks=None, B=0):
+        return f(P, qs, P, ks, P, None, P, None, None, B, 8, 2, 16, 16, 128, 1, 0, 0.1, None)
+    assert call() == OK                                   # NULL strides: contiguous
+    assert call(qs=_st(16 * 8 * 128, 8 * 128, 128)) == OK  # explicit dense strides
+    assert call(qs=_st(16 * 8 * 128, 8 * 128, 12)) == INVALID    # head stride not a multiple of 8
+    assert call(qs=_st(-8, 8 * 128, 128)) == INVALID              # negative
+    assert call(ks=_st(0, 1 << 24, 128)) == INVALID               # K token stride too large
+    assert call(ks=_st(0, (1 << 24) - 8, 128)) == OK
+
+
+def test_strided_decode_validation(lib):
+    f = lib.fa_decode_paged_strided
+    def call(ks=None, os_=None, B=0):
+        return f(P, None, P, ks, P, None, P, P, P, os_, None, B, 1, 8, 2, 128, 64, 16, 8, 64, 1, 0,
+                 0.1, P, 1 << 30, None)
+    assert call() == OK
+    assert call(ks=_st(2 * 16 * 2 * 128, 2 * 2 * 128, 128)) == OK      # K/V interleaved per slot
+    assert call(ks=_st(4, 8, 8)) == INVALID
+    assert call(os_=_st(8, 8, -8)) == INVALID
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=80), UNSUPPORTED), (dict(page_size=3), UNSUPPORTED), (dict(Hkv=0), INVALID),
+    (dict(num_pages=0), INVALID), (dict(lens=None), INVALID), (dict(kc=P + 4), INVALID),
+    (dict(kn=None), INVALID), (dict(ks=_st(0, 12, 8)), INVALID),
+    (dict(B=0), OK), (dict(Snew=0), OK), (dict(table=None, num_pages=0, B=0), OK),
+])
+def test_kv_append_validation(lib, kw, want):
+    a = dict(kc=P, ks=None, vc=P, vs=None, table=P, lens=P, kn=P, kns=None, vn=P, vns=None,
+             B=2, Snew=4, Hkv=2, D=128, num_pages=64, page_size=16, max_pages=8)
+    a.update(kw)
+    assert lib.fa_kv_append(a["kc"], a["ks"], a["vc"], a["vs"], a["table"], a["lens"], a["kn"], a["kns"],
+                            a["vn"], a["vns"], a["B"], a["Snew"], a["Hkv"], a["D"], a["num_pages"],
+                            a["page_size"], a["max_pages"], None) == want
