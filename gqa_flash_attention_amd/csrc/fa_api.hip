@@ -97,7 +97,7 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
   if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0) return 0;
-  const int64_t slots = (int64_t)kSlotsPerChunk * n_chunks_for(max_seq_len, kv_chunk);
+  const int64_t slots = n_chunks_for(max_seq_len, kv_chunk) + 1;
   const int64_t rows = (int64_t)B * Hq * Sq;
   const size_t o_bytes = align256((size_t)(rows * slots * D) * sizeof(float));
   const size_t l_bytes = align256((size_t)(rows * slots) * sizeof(float));
@@ -140,7 +140,7 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return FA_ERR_WORKSPACE;
   const int64_t max_chunks = n_chunks_for(max_len, kv_chunk);
-  const int64_t n_slots = (int64_t)kSlotsPerChunk * max_chunks;
+  const int64_t n_slots = max_chunks + 1;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   // the split kernel counts tiles (at most one per 32 keys plus one per
   // chunk, per block of 32 rows and KV head) in 32-bit integers
@@ -160,8 +160,7 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
-  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)kSlotsPerChunk, (int)n_slots,
-                 o, lse, os, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, B, Sq, Hq, D};
   return to_status(launch_combine(cd, st));
 }
 
@@ -189,7 +188,7 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
   const Strides od{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
-  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, 1, max_chunks, o, lse, od, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, od, B, Sq, Hq, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
 }
 

@@ -49,10 +49,11 @@
 // until the end and none idles in a tail (the Stream-K way of balancing a
 // split reduction), and the Hkv workgroups of a set read the same token rows
 // ([.., Hkv, D] is token-major) side by side. Keys are cut into chunks of
-// kv_chunk tokens; every partial covers all or part of one chunk, tiles never
-// straddle a chunk, and a chunk cut by workgroup boundaries leaves one
-// partial per piece (slots 4c .. 4c + 3, the unused ones marked empty) that
-// the LSE combine merges like any others.
+// kv_chunk tokens, the unit of the split: tiles never straddle a chunk and a
+// range holds at least one chunk. A range merges the chunks it holds in its
+// online softmax (an incremental LSE combine) and writes one partial per
+// block of rows it touches, in slot r - r0 of those rows (r the range, r0 the
+// range of the rows' first tile); the LSE combine merges the partials.
 #pragma once
 
 #include "fa_device.h"
@@ -83,7 +84,7 @@ struct AttnArgs {
   int causal, window;
   float sl2;              // scale * log2(e)
   int n_rb;               // row blocks per (b, g)
-  int chunk, n_slots;     // split mode: keys per chunk, partial slots per row (kSlotsPerChunk per chunk)
+  int chunk, n_slots;     // split mode: keys per chunk, partial slots per row (chunks + 1)
 };
 
 // Spread a 1-D grid over the 8 XCDs so that logical neighbours (row blocks of
@@ -317,6 +318,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   int b = 0;
   int p = 0, wpmin = 0, wpmax = 0, qi = 0, qh = 0;
   bool row_ok = false;
+  bool wave_rows = false;      // this wave holds at least one row (uniform per wave)
   int ke = 0;                  // end (exclusive) of the keys the current tile may hold
   bf16x8 qf[NQC];
   auto set_rows = [&](int b_, int g_, int rb_, int n_keys) {
@@ -329,6 +331,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const int wr_hi = min(wr_lo + 32, r_hi);
     wpmin = wr_lo / a.G + shift;
     wpmax = (wr_hi - 1) / a.G + shift;
+    wave_rows = wr_lo < r_hi;
     const int r = wr_lo + j;
     row_ok = r < r_hi;
     qi = row_ok ? r / a.G : 0;
@@ -457,6 +460,56 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         oacc[db] = mfma32(as_bf16x8(vw), as_bf16x8(pf[ks]), oacc[db]);
       }
     }
+  };
+
+  // Register-staged forms, used by the one-wave split kernel: a tile's operand
+  // fragments are first read out of LDS, so its buffer can be refilled before
+  // the MFMAs run. Same addresses as scores/accumulate above.
+  auto read_k = [&](const uint16_t* bk, u32x4 (&kr)[NQC][NKB]) {
+#pragma unroll
+    for (int c = 0; c < NQC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = 32 * kb + j;
+        const int ch = 2 * (c + dh * NQC) + hl;
+        kr[c][kb] = *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
+      }
+  };
+  // S^T from registers; even and odd d steps feed two accumulators so that
+  // the dependent MFMA chain is half as long.
+  auto scores_regs = [&](const u32x4 (&kr)[NQC][NKB], f32x16 (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 s0{}, s1{};
+#pragma unroll
+      for (int c = 0; c < NQC; c += 2) {
+        s0 = mfma32(as_bf16x8(kr[c][kb]), qf[c], s0);
+        if (c + 1 < NQC) s1 = mfma32(as_bf16x8(kr[c + 1][kb]), qf[c + 1], s1);
+      }
+      s[kb] = s0 + s1;
+    }
+  };
+  auto read_v = [&](const uint16_t* bv, u32x4 (&vr)[NKS][NDB]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
+        const int dch = d >> 3, dsub = d & 7;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int row = 16 * ks + 8 * half + 4 * hl + (m16 >> 2);
+          const u32x2 t = read_tr16(&bv[row * D + 8 * (dch ^ swz_v<D>(row)) + dsub]);
+          vr[ks][db][2 * half] = t[0];
+          vr[ks][db][2 * half + 1] = t[1];
+        }
+      }
+  };
+  auto accumulate_regs = [&](const u32x4 (&vr)[NKS][NDB], const u32x4 (&pf)[NKS]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(as_bf16x8(vr[ks][db]), as_bf16x8(pf[ks]), oacc[db]);
   };
 
   // D split: publish this wave's partial scores, and add the group's.
@@ -598,7 +651,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         if (row_span<BN, BM>(a, len, r, tpc).nt > 0) continue;
         for (int gg = 0; gg < a.Hkv; ++gg) {
           set_rows(bb, gg, r, len);
-          write_empty(0, kSlotsPerChunk * nch);
+          write_empty(0, nch + 1);
         }
       }
     }
@@ -607,10 +660,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // (the grid is a multiple of Hkv workgroups)
     const int g_w = w % a.Hkv;
     const int sets = W / a.Hkv;
-    // a chunk (at most tpc tiles) must meet at most SPC ranges
-    constexpr int SPC = kSlotsPerChunk;
-    const int per_min = max((tpc - 1 + SPC - 2) / (SPC - 1), 1);
-    const int per = (int)max(((int64_t)T + sets - 1) / sets, (int64_t)per_min);
+    // a range holds at least one chunk, so the rows of a sequence meet at
+    // most (its chunks + 1) ranges
+    const int per = (int)max(((int64_t)T + sets - 1) / sets, (int64_t)tpc);
     const int64_t x0l = (int64_t)(w / a.Hkv) * per;
     if (x0l >= T) return;
     const int x0 = (int)x0l;
@@ -687,18 +739,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
     auto tile_tb = [&](const It& t) -> int { return t.c * C + t.k * BN; };
     auto tile_ke = [&](const It& t) -> int { return (int)min((int64_t)(t.c + 1) * C, (int64_t)t.len); };
-    auto last_of_chunk = [&](const It& t) -> bool { return t.c == t.c_hi ? t.k == t.k1 : t.k == tpc - 1; };
     auto n_chunks = [&](const It& t) -> int { return (int)(((int64_t)t.len + C - 1) / C); };
 
     set_rows(cu.b, g_w, cu.rb, cu.len);
     // a row's first tile also marks the chunks before its visible keys empty
-    if (cu.i == 0) write_empty(0, SPC * cu.c_lo);
-    // Global index of the current chunk's first tile; the piece of the chunk
-    // in range r (ranges are [r per, (r + 1) per)) fills slot SPC c + r - r0,
-    // with r0 the range of that first tile.
-    int cfx = x0 - (cu.k - (cu.c == cu.c_lo ? cu.k0 : 0));
-    int part = x0 / per - cfx / per;
-
+    // This range's slot in the rows' partials: ranges are [r per, (r + 1)
+    // per); the rows' first tile (global index x_first) lies in range r0.
+    int slot = x0 / per - (x0 - cu.i) / per;
     // ---- copy pipeline --------------------------------------------------------
     // The loop keeps as many copies in flight as the ring holds instead of
     // overlapping MFMA and softmax. Each buffer is refilled as soon as its
@@ -711,6 +758,28 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // earlier, so one descriptor (key start, key end, V base, sequence) of
     // that tile is kept.
     constexpr int AHEAD_CP = 2 * (NBUF - 1) * SEGW < 63 ? 2 * (NBUF - 1) * SEGW : 63;
+    // One-wave workgroups read each tile into registers as soon as it lands
+    // and refill its buffer at once (the refill then does not wait for the
+    // tile's MFMAs and softmax): per step K(t + NBUF) right after K(t) is
+    // read, V(t + NBUF) right after V(t) is read, so at every wait 2 NBUF - 1
+    // of the 2 NBUF buffers are being filled.
+    constexpr bool EARLY = NW == 1;
+    constexpr int AHEAD_E = (2 * NBUF - 1) * SEGW < 63 ? (2 * NBUF - 1) * SEGW : 63;
+    // Stores count in vmcnt too, in issue order with the copies. The NDB * 4
+    // vector stores of a partial output, issued after tile t, are younger than
+    // the copies the next four waits target (K(t+1), V(t+1), K(t+2), V(t+2)),
+    // so those waits also allow them; without this each partial write would
+    // drain the copy ring. Any other store or load issued meanwhile only makes
+    // a wait stricter, never looser.
+    constexpr int ST_PART = NDB * 4;
+    constexpr int AHEAD_ES = AHEAD_E + ST_PART < 63 ? AHEAD_E + ST_PART : 63;
+    int boost = 0;                                   // waits left that allow the stores
+    auto wait_e = [&](bool deep) {
+      if (!deep) wait_vm<0>();
+      else if (boost > 0) wait_vm<AHEAD_ES>();
+      else wait_vm<AHEAD_E>();
+      boost = boost > 0 ? boost - 1 : 0;
+    };
     It pf = cu;
     int d_tb = 0, d_ke = 0, d_b = 0;
     const uint16_t* d_vb = nullptr;
@@ -730,62 +799,90 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         if (jj + 1 < n_loc) it_next(pf);
       }
     }
-    auto sstep = [&](int it, int u) {
-      const bool deep = it + NBUF - 1 < n_loc;   // uniform: a full ring behind this tile
-      // K(t) landed in every wave's share; every wave is done with the PV
-      // product of tile t-1, whose V buffer is refilled next
-      if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
-      __syncthreads();
-      if (it >= 1 && it + NBUF - 1 < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf((u + NBUF - 1) % NBUF));
-      const int tb = tile_tb(cu);
-      ke = tile_ke(cu);
-      f32x16 sc[NKB];
-      scores(kbuf(u), sc);
-      if constexpr (DS > 1) {
-        publish(sc, it & 1);
-        __syncthreads();
-        combine_partner(sc, it & 1);
-      }
-      const float nb = prepare(sc, tb);
-      u32x4 pv[NKS];
-      exponentiate(sc, nb, pv);
-      // V(t) landed; every wave is done with K(t), whose buffer is refilled
-      if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
-      __syncthreads();
-      if (it + NBUF < n_loc) {
-        issue_next_k(kbuf(u));
-        if (it + NBUF + 1 < n_loc) it_next(pf);
-      }
-      accumulate(vbuf(u), pv);
-
-      // ---- after the tile: close the partial if its chunk or rows end here ---
-      // The rows change exactly after their last tile; inside the rows the
-      // chunk changes exactly after its last tile.
+    // ---- after a tile: close the partial if its chunk or rows end here ------
+    // The rows change exactly after their last tile; inside the rows the
+    // chunk changes exactly after its last tile.
+    // ---- after a tile: close the partial if the range or the rows end here --
+    // The chunks of a range merge in the running softmax; the rows change
+    // exactly after their last tile.
+    auto finish_tile = [&](int it) {
       const bool range_end = it + 1 == n_loc;
       const bool rows_end = cu.i == cu.nt - 1;
-      const bool chunk_end = last_of_chunk(cu);
-      if (range_end || chunk_end) {
-        write_partial(SPC * cu.c + part);
-        if (part == 0) {
-          // the range holding the chunk's first tile marks the slots its
-          // pieces do not use empty
-          const int last = (cu.c == cu.c_hi ? cu.k1 : tpc - 1) - (cu.c == cu.c_lo ? cu.k0 : 0);
-          const int pieces = (cfx + last) / per - cfx / per + 1;
-          write_empty(SPC * cu.c + pieces, SPC * cu.c + SPC);
-        }
-        // the rows' last tile marks the chunks after their visible keys empty
-        if (rows_end) write_empty(SPC * (cu.c_hi + 1), SPC * n_chunks(cu));
+      if (range_end || rows_end) {
+        write_partial(slot);
+        // the range holding the rows' last tile marks their unused slots
+        // (up to chunks + 1) empty
+        if (rows_end) write_empty(slot + 1, n_chunks(cu) + 1);
         reset_state();
-        part = 0;
-        cfx = x0 + it + 1;                       // the next tile starts a chunk
+        if (EARLY) boost = wave_rows ? 4 : 0;      // ST_PART stores issued (none without rows)
       }
       if (!range_end) {
         it_next(cu);
         if (rows_end) {
           set_rows(cu.b, g_w, cu.rb, cu.len);
-          write_empty(0, SPC * cu.c_lo);
+          slot = 0;                                // the rows start inside this range
         }
       }
+    };
+    auto sstep = [&](int it, int u) {
+      const int tb = tile_tb(cu);
+      if constexpr (EARLY) {
+        // K(t) landed (copies issued after it: V(t) and the tiles behind)
+        wait_e(it + NBUF - 1 < n_loc);
+        __syncthreads();
+        u32x4 kr[NQC][NKB];
+        read_k(kbuf(u), kr);
+        wait_lgkm0();
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + NBUF < n_loc) {
+          issue_next_k(kbuf(u));
+          if (it + NBUF + 1 < n_loc) it_next(pf);
+        }
+        ke = tile_ke(cu);
+        f32x16 sc[NKB];
+        scores_regs(kr, sc);
+        const float nb = prepare(sc, tb);
+        u32x4 pv[NKS];
+        exponentiate(sc, nb, pv);
+        // V(t) landed (copies issued after it: the tiles behind and K(t + NBUF))
+        wait_e(it + NBUF < n_loc);
+        __syncthreads();
+        u32x4 vr[NKS][NDB];
+        read_v(vbuf(u), vr);
+        wait_lgkm0();
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + NBUF < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf(u));
+        accumulate_regs(vr, pv);
+      } else {
+        // The copy order after the prologue is, per step t, V(t + NBUF - 1)
+        // (refilling tile t-1's V buffer) then K(t + NBUF).
+        const bool deep = it + NBUF - 1 < n_loc;   // uniform: a full ring behind this tile
+        // K(t) landed in every wave's share; every wave is done with the PV
+        // product of tile t-1, whose V buffer is refilled next
+        if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
+        __syncthreads();
+        if (it >= 1 && it + NBUF - 1 < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf((u + NBUF - 1) % NBUF));
+        ke = tile_ke(cu);
+        f32x16 sc[NKB];
+        scores(kbuf(u), sc);
+        if constexpr (DS > 1) {
+          publish(sc, it & 1);
+          __syncthreads();
+          combine_partner(sc, it & 1);
+        }
+        const float nb = prepare(sc, tb);
+        u32x4 pv[NKS];
+        exponentiate(sc, nb, pv);
+        // V(t) landed; every wave is done with K(t), whose buffer is refilled
+        if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
+        __syncthreads();
+        if (it + NBUF < n_loc) {
+          issue_next_k(kbuf(u));
+          if (it + NBUF + 1 < n_loc) it_next(pf);
+        }
+        accumulate(vbuf(u), pv);
+      }
+      finish_tile(it);
     };
     for (int it = 0; it < n_loc; it += NBUF) {
 #pragma unroll

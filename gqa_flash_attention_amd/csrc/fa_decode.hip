@@ -2,10 +2,10 @@
 // the paged-gather test hook.
 //
 // Split-KV: a persistent grid, one workgroup per slot the GPU holds at once,
-// streams all K/V tiles in equal contiguous ranges and writes fp32 partial
-// outputs normalised by their own row sums plus the row LSEs, at most two per
-// chunk of kv_chunk keys; the combine kernel merges the partials of a row by
-// their LSE (beellama.cpp PR 149: a combine kernel runs after the split blocks
+// streams all K/V tiles in equal contiguous ranges (whole tiles of chunks of
+// kv_chunk keys) and writes one fp32 partial output per range and block of
+// rows, normalised by its own row sum, plus the row LSEs; the combine kernel
+// merges the partials of a row by their LSE (beellama.cpp PR 149: a combine kernel runs after the split blocks
 // when the KV range is split into parallel blocks, on the same stream, and
 // every partial must publish its (max, rowsum)).
 #include <algorithm>
@@ -23,7 +23,9 @@ template <int D, int NWR> struct SplitCfg {
   static constexpr int DS = D >= 512 ? 4 : (D >= 256 ? 2 : 1);
   static constexpr int NW = NWR * DS;
   static constexpr int BN = 32;
-  static constexpr int WPE = D <= 128 ? 2 : 1;
+  // waves per SIMD the registers are sized for: one-wave workgroups (four
+  // per CU, held by LDS) run one wave per SIMD and stage tiles in registers
+  static constexpr int WPE = (D <= 128 && NW > 1) ? 2 : 1;
   // tile buffers per operand: two keep 3/4 of the ring in flight; larger
   // head dims are LDS-bound
   static constexpr int NBUF = 2;
@@ -110,7 +112,7 @@ struct CombineArgs {
   const float* lse_part;
   const int32_t* n_chunks;
   const int32_t* seq_lens;
-  int kv_chunk, slots_per_chunk, n_slots;
+  int kv_chunk, n_slots;
   uint16_t* o;
   float* lse;
   int64_t o_sb, o_ss, o_sh;     // element strides of o (sequence, row, head)
@@ -157,7 +159,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
     n = c.n_chunks[b];
   } else if (c.seq_lens != nullptr) {
     const int len = max(c.seq_lens[b], 0);
-    n = (int)((((int64_t)len + c.kv_chunk - 1) / c.kv_chunk) * c.slots_per_chunk);
+    n = len > 0 ? (int)(((int64_t)len + c.kv_chunk - 1) / c.kv_chunk) + 1 : 0;
   }
   n = max(0, min(n, c.n_slots));
 
@@ -253,7 +255,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
 
 template <int D>
 hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
-  CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.slots_per_chunk, d.n_slots,
+  CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.n_slots,
                 static_cast<uint16_t*>(d.o), d.lse, d.os.outer, d.os.token, d.os.head, d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
   if (rows == 0) return hipSuccess;

@@ -116,6 +116,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
+// Wait until every LDS (and scalar-memory) access of this wave has completed:
+// s_waitcnt lgkmcnt(0), leaving vmcnt and expcnt at their maxima.
+__device__ __forceinline__ void wait_lgkm0() {
+  constexpr int imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
 // Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16). Within
 // each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows
 // addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 (in that

@@ -6,10 +6,6 @@
 
 namespace gqafa {
 
-// Split-KV partial slots per chunk of kv_chunk keys: the balanced split cuts
-// a chunk between at most this many workgroups, each leaving one partial.
-constexpr int kSlotsPerChunk = 4;
-
 // Element strides of a [B, S, H, D] tensor (or a paged cache [pages, slots,
 // H, D]): outer (batch or page), token (or slot), head; D is unit-stride.
 struct Strides {
@@ -26,7 +22,7 @@ struct PrefillDesc {
 struct SplitDesc {
   const void* q; const void* kcache; const void* vcache;
   const int32_t* table; const int32_t* seq_lens;
-  float* o_part; float* lse_part;   // [B, Hq, Sq, n_slots(, D)]: kSlotsPerChunk per chunk
+  float* o_part; float* lse_part;   // [B, Hq, Sq, n_slots(, D)]: chunks + 1 slots per row
   Strides qs, ks, vs;
   int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, n_slots, causal, window;
   float scale;
@@ -35,8 +31,8 @@ struct SplitDesc {
 struct CombineDesc {
   const float* o_part; const float* lse_part;
   const int32_t* n_chunks;   // device [B] or null: partials to merge per sequence
-  const int32_t* seq_lens;   // used when n_chunks is null: slots_per_chunk * ceil(len / kv_chunk)
-  int kv_chunk, slots_per_chunk, n_slots;   // n_slots: slots per row in memory
+  const int32_t* seq_lens;   // used when n_chunks is null: ceil(len / kv_chunk) + 1 slots (0 if len = 0)
+  int kv_chunk, n_slots;     // n_slots: slots per row in memory
   void* o; float* lse;
   Strides os;                // o [B, Sq, Hq, D]
   int B, Sq, Hq, D;

@@ -91,9 +91,9 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
 /*
  * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
  * [B, Hq, Sq, n_slots, D] and their LSEs [B, Hq, Sq, n_slots], with
- * n_slots = 4 * ceil(max_seq_len / kv_chunk) (the balanced split cuts a
- * chunk between at most four workgroups, each leaving one partial), each
- * region 256-byte aligned. Returns 0 for invalid sizes.
+ * n_slots = ceil(max_seq_len / kv_chunk) + 1 (a sequence's keys meet at most
+ * that many workgroup ranges of the balanced split), each region 256-byte
+ * aligned. Returns 0 for invalid sizes.
  */
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk);
 
@@ -102,8 +102,9 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
  * them) over a paged KV cache, split over the KV sequence in chunks of
  * kv_chunk tokens and merged by LSE (split-KV, "parallel blocks" + combine:
  * beellama.cpp PR 149, Overview). The split kernel is a persistent grid that
- * gives every workgroup an equal share of all K/V tiles; each partial covers
- * all or part of one chunk.
+ * gives every workgroup an equal, contiguous range of all K/V tiles (at least
+ * one chunk; tiles never straddle a chunk); a range merges its chunks in its
+ * online softmax and leaves one partial per block of rows it touches.
  *
  *   q           bf16 [B, Sq, Hq, D]: the Sq newest rows of each sequence
  *   kcache      bf16 [num_pages, page_size, Hkv, D] when block_table != NULL;

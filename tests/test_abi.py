@@ -104,15 +104,15 @@ def test_decode_validation(lib, kw, want):
 
 def test_workspace_bytes(lib):
     f = lib.fa_decode_workspace_bytes
-    # C3 shape: 16 x 32 rows x (4 x 64 chunk slots) x (128 + 1) fp32
-    assert f(16, 1, 32, 128, 16384, 256) == 16 * 32 * 256 * 128 * 4 + 16 * 32 * 256 * 4
+    # C3 shape: 16 x 32 rows x (64 chunks + 1 slots) x (128 + 1) fp32
+    assert f(16, 1, 32, 128, 16384, 256) == 16 * 32 * 65 * 128 * 4 + 16 * 32 * 65 * 4
     assert f(1, 1, 1, 96, 10, 4) == 0          # unsupported head dim
     assert f(1, 1, 1, 64, 10, 0) == 0          # bad chunk
 
 
 def test_workspace_bytes_alignment(lib):
     f = lib.fa_decode_workspace_bytes
-    rows, slots, D = 1 * 2 * 3, 4 * 3, 64
+    rows, slots, D = 1 * 2 * 3, 3 + 1, 64
     o = rows * slots * D * 4
     l = rows * slots * 4
     up = lambda x: (x + 255) // 256 * 256

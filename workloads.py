@@ -76,7 +76,7 @@ C4B = PrefillShape("prefill_c4b", B=1, Hq=16, Hkv=8, Sq=8192, Skv=8192, D=512, s
 C3 = DecodeShape("decode_c3", B=16, Sq=1, Hq=32, Hkv=8, D=128, page_size=0, max_len=16384,
                  len_lo=1024, len_hi=16384, kv_chunk=256, seed=1003)
 C5 = DecodeShape("verify_c5", B=4, Sq=8, Hq=64, Hkv=8, D=128, page_size=16, max_len=32768,
-                 len_lo=32768, len_hi=32768, kv_chunk=2048, seed=1005)
+                 len_lo=32768, len_hi=32768, kv_chunk=1024, seed=1005)
 
 WORKLOADS = {w.name: w for w in (C1, C2, C3, C4A, C4B, C5)}
 
