@@ -758,12 +758,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // earlier, so one descriptor (key start, key end, V base, sequence) of
     // that tile is kept.
     constexpr int AHEAD_CP = 2 * (NBUF - 1) * SEGW < 63 ? 2 * (NBUF - 1) * SEGW : 63;
-    // One-wave workgroups read each tile into registers as soon as it lands
-    // and refill its buffer at once (the refill then does not wait for the
-    // tile's MFMAs and softmax): per step K(t + NBUF) right after K(t) is
-    // read, V(t + NBUF) right after V(t) is read, so at every wait 2 NBUF - 1
-    // of the 2 NBUF buffers are being filled.
-    constexpr bool EARLY = NW == 1;
+    // Without a D split the waves read each tile into registers as soon as
+    // it lands and the buffer is refilled once all have read it (the refill
+    // then does not wait for the tile's MFMAs and softmax): per step
+    // K(t + NBUF) right after K(t) is read, V(t + NBUF) right after V(t) is
+    // read, so at every wait 2 NBUF - 1 of the 2 NBUF buffers are being
+    // filled.
+    constexpr bool EARLY = DS == 1;
     constexpr int AHEAD_E = (2 * NBUF - 1) * SEGW < 63 ? (2 * NBUF - 1) * SEGW : 63;
     // Stores count in vmcnt too, in issue order with the copies. The NDB * 4
     // vector stores of a partial output, issued after tile t, are younger than
@@ -833,6 +834,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         u32x4 kr[NQC][NKB];
         read_k(kbuf(u), kr);
         wait_lgkm0();
+        if constexpr (NW > 1) __syncthreads();     // every wave has read K(t)
         __builtin_amdgcn_sched_barrier(0);
         if (it + NBUF < n_loc) {
           issue_next_k(kbuf(u));
@@ -850,6 +852,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         u32x4 vr[NKS][NDB];
         read_v(vbuf(u), vr);
         wait_lgkm0();
+        if constexpr (NW > 1) __syncthreads();     // every wave has read V(t)
         __builtin_amdgcn_sched_barrier(0);
         if (it + NBUF < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf(u));
         accumulate_regs(vr, pv);

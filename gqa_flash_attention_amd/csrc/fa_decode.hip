@@ -24,7 +24,7 @@ template <int D, int NWR> struct SplitCfg {
   static constexpr int NW = NWR * DS;
   static constexpr int BN = 32;
   // waves per SIMD the registers are sized for: one-wave workgroups (four
-  // per CU, held by LDS) run one wave per SIMD and stage tiles in registers
+  // per CU, held by LDS) run one wave per SIMD; two- and four-wave ones two
   static constexpr int WPE = (D <= 128 && NW > 1) ? 2 : 1;
   // tile buffers per operand: two keep 3/4 of the ring in flight; larger
   // head dims are LDS-bound
