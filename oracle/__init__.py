@@ -5,6 +5,7 @@ leg may import this package. It shares no code with the HIP path.
 """
 
 from .attention import (  # noqa: F401
+    alibi_slopes,
     attention_ref,
     combine_ref,
     decode_paged_ref,

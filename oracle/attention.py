@@ -37,6 +37,23 @@ in the design notes of the repository):
   exp(LSE_c - LSE) O_c, with M = max_c LSE_c. A chunk with LSE_c = -inf has
   weight 0; when every chunk is empty the row is O = 0, LSE = -inf.
 
+Score modifiers, named (without their formulas) by the FLASH_ATTN_EXT case
+parameters of the llama.cpp PR 28507 test report (mask, sinks, max_bias,
+logit_softcap); the formulas are readings of this build:
+
+* logit_softcap c > 0: the scaled score s = scale * q . k becomes
+  c * tanh(s / c).
+* max_bias > 0 (ALiBi): query head h adds slope_h * (j - p_i) to the score
+  of key j, with n = 2^floor(log2 Hq), m0 = 2^(-max_bias / n),
+  m1 = 2^(-max_bias / (2 n)), slope_h = m0^(h + 1) for h < n and
+  m1^(2 (h - n) + 1) otherwise (the geometric slopes of ALiBi).
+* sinks: one extra logit sink_h per query head joins the softmax
+  denominator and carries no value: l = sum_j exp(s_j) + exp(sink_h),
+  O = sum_j exp(s_j) v_j / l, LSE = ln l. A row with no visible key then has
+  O = 0 and LSE = sink_h.
+
+The softcap applies first, then the ALiBi bias, then the mask.
+
 Every floating-point value is widened to float64 before any arithmetic.
 """
 
@@ -53,6 +70,7 @@ __all__ = [
     "partial_attention_ref",
     "combine_ref",
     "kv_append_ref",
+    "alibi_slopes",
 ]
 
 
@@ -87,24 +105,42 @@ def visible_mask(rows: np.ndarray, sq: int, skv: int, causal: bool, window: int)
     return vis
 
 
-def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float):
+def alibi_slopes(hq: int, max_bias: float) -> np.ndarray:
+    """ALiBi slope of each of hq query heads (all zero when max_bias <= 0)."""
+    if max_bias <= 0:
+        return np.zeros(hq)
+    n = 1 << int(np.floor(np.log2(hq)))
+    m0 = 2.0 ** (-max_bias / n)
+    m1 = 2.0 ** (-max_bias / (2.0 * n))
+    return np.array([m0 ** (h + 1) if h < n else m1 ** (2 * (h - n) + 1) for h in range(hq)])
+
+
+def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float,
+                 softcap: float = 0.0, bias=None, sink: float = -np.inf):
     """Two-pass softmax attention for a block of rows of one query head.
 
-    q_rows [R, D], k and v [S, D], vis [R, S] boolean. Returns O [R, D] and
+    q_rows [R, D], k and v [S, D], vis [R, S] boolean; optional softcap,
+    additive bias [R, S] (ALiBi) and sink logit. Returns O [R, D] and
     LSE [R], both float64.
 
-    Pass 1 takes the maximum score over the visible keys of each row; pass 2
-    sums exp(score - max) and the same weights times V.
+    Pass 1 takes the maximum over the visible scores of each row (and the
+    sink); pass 2 sums exp(score - max), plus exp(sink - max), and the
+    score weights times V.
     """
     s = scale * (q_rows @ k.T)                      # scores, [R, S]
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
+    if bias is not None:
+        s = s + bias
     s = np.where(vis, s, -np.inf)
-    # pass 1: row maximum over visible keys (-inf when a row sees no key)
+    # pass 1: row maximum over visible keys and the sink (-inf when neither)
     m = np.max(s, axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
+    m = np.maximum(m, sink)
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
-    # pass 2: exponent sum and weighted sum of V
+    # pass 2: exponent sum (with the sink's term) and weighted sum of V
     e = np.exp(s - m_safe[:, None])                 # masked keys give exp(-inf) = 0
-    l = e.sum(axis=1)
+    l = e.sum(axis=1) + np.exp(sink - m_safe)
     num = e @ v
     with np.errstate(invalid="ignore", divide="ignore"):
         o = np.where(empty[:, None], 0.0, num / np.where(empty, 1.0, l)[:, None])
@@ -113,7 +149,8 @@ def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarr
 
 
 def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
-                  seq_lens=None, rows=None, heads=None, batches=None, row_block: int = 512):
+                  seq_lens=None, rows=None, heads=None, batches=None, row_block: int = 512,
+                  softcap: float = 0.0, max_bias: float = 0.0, sinks=None):
     """Reference attention for grouped-query heads.
 
     q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D] (numpy or CPU torch, any float
@@ -121,7 +158,9 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
     Skv_b <= Skv per sequence; keys at or beyond it are ignored. rows, heads
     and batches optionally restrict which query rows / query heads /
     sequences are computed (for sampling at large sizes); the result still
-    has the full shape and the rows not computed hold NaN.
+    has the full shape and the rows not computed hold NaN. softcap,
+    max_bias and sinks ([Hq] logits or None) are the score modifiers of the
+    module docstring (all off by default).
 
     Returns O [B, Sq, Hq, D] and LSE [B, Hq, Sq] in float64.
     """
@@ -140,6 +179,8 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
     heads = range(Hq) if heads is None else heads
     batches = range(B) if batches is None else batches
 
+    slopes = alibi_slopes(Hq, max_bias)
+    sink_v = None if sinks is None else to_f64(sinks).reshape(-1)
     o = np.full((B, Sq, Hq, D), np.nan)
     lse = np.full((B, Hq, Sq), np.nan)
     for b in batches:
@@ -152,7 +193,12 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
             for r0 in range(0, rows.size, row_block):
                 rr = rows[r0:r0 + row_block]
                 vis = visible_mask(rr, Sq, skv, causal, window)
-                ob, lb = _attend_rows(q[b, rr, h, :], kb, vb, vis, scale)
+                bias = None
+                if max_bias > 0:
+                    pos = rr + (skv - Sq)            # absolute positions of the rows
+                    bias = slopes[h] * (np.arange(skv)[None, :] - pos[:, None])
+                sink = -np.inf if sink_v is None else float(sink_v[h])
+                ob, lb = _attend_rows(q[b, rr, h, :], kb, vb, vis, scale, softcap, bias, sink)
                 o[b, rr, h, :] = ob
                 lse[b, h, rr] = lb
     return o, lse
@@ -185,7 +231,8 @@ def paged_gather_ref(cache, block_table, seq_lens, page_size: int, max_len: int 
 
 
 def decode_paged_ref(q, kcache, vcache, block_table, seq_lens, *, page_size: int,
-                     causal: bool, window: int = 0, scale: float, rows=None, heads=None):
+                     causal: bool, window: int = 0, scale: float, rows=None, heads=None,
+                     softcap: float = 0.0, max_bias: float = 0.0, sinks=None):
     """Reference decode / speculative verify over a paged (or contiguous) cache.
 
     q [B, Sq, Hq, D] holds the Sq newest query rows of each sequence (Sq = 1
@@ -203,7 +250,8 @@ def decode_paged_ref(q, kcache, vcache, block_table, seq_lens, *, page_size: int
         k = paged_gather_ref(kcache, block_table, lens, page_size, max_len)
         v = paged_gather_ref(vcache, block_table, lens, page_size, max_len)
     return attention_ref(q, k, v, causal=causal, window=window, scale=scale,
-                         seq_lens=lens, rows=rows, heads=heads)
+                         seq_lens=lens, rows=rows, heads=heads, softcap=softcap,
+                         max_bias=max_bias, sinks=sinks)
 
 
 def partial_attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
@@ -244,11 +292,13 @@ def partial_attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: floa
     return o, lse
 
 
-def combine_ref(o_part, lse_part, n_chunks=None):
+def combine_ref(o_part, lse_part, n_chunks=None, sinks=None):
     """Merge split-KV partials by their log-sum-exp.
 
     o_part [B, Hq, Sq, C, D], lse_part [B, Hq, Sq, C]; n_chunks (optional,
     length B) limits how many leading chunks of sequence b are merged.
+    sinks ([Hq] or None) adds each head's sink as one more partial with
+    LSE = sink_h and O = 0 (its logit joins the denominator, no value).
     Returns O [B, Sq, Hq, D] and LSE [B, Hq, Sq] in float64.
     """
     o_part = to_f64(o_part)
@@ -256,6 +306,21 @@ def combine_ref(o_part, lse_part, n_chunks=None):
     B, Hq, Sq, C, D = o_part.shape
     if n_chunks is None:
         n_chunks = [C] * B
+    if sinks is not None:
+        sk = to_f64(sinks).reshape(1, Hq, 1, 1) * np.ones((B, Hq, Sq, 1))
+        o_part = np.concatenate([o_part, np.zeros((B, Hq, Sq, 1, D))], axis=3)
+        # the sink goes right after each sequence's merged chunks
+        lp = np.full((B, Hq, Sq, C + 1), -np.inf)
+        for b in range(B):
+            n = max(0, min(int(n_chunks[b]), C))
+            lp[b, :, :, :n] = lse_part[b, :, :, :n]
+            lp[b, :, :, n] = sk[b, :, :, 0]
+            o_part[b, :, :, n, :] = 0.0
+            if n < C:
+                o_part[b, :, :, n + 1:, :] = 0.0
+        lse_part = lp
+        n_chunks = [max(0, min(int(x), C)) + 1 for x in n_chunks]
+        C = C + 1
     o = np.zeros((B, Sq, Hq, D))
     lse = np.full((B, Hq, Sq), -np.inf)
     for b in range(B):

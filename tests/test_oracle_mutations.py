@@ -8,6 +8,7 @@ import types
 import pytest
 
 from tests.oracle_pins import ALL_CHECKS
+from tests.test_oracle_mods import MOD_CHECKS
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
 
@@ -24,6 +25,20 @@ MUTATIONS = {
     "gather slot index": ("out[b, t] = cache[page, t % page_size]", "out[b, t] = cache[page, t // page_size % page_size]"),
     "seq_lens ignored": ("skv = seq_lens[b]", "skv = Skv"),
     "empty row lse": ("lse = np.where(empty, -np.inf,", "lse = np.where(empty, 0.0,"),
+    'softcap after bias': ('    if softcap > 0:\n        s = softcap * np.tanh(s / softcap)\n    if bias is not None:\n        s = s + bias',
+        '    if bias is not None:\n        s = s + bias\n    if softcap > 0:\n        s = softcap * np.tanh(s / softcap)'),
+    'softcap without inner division': ('s = softcap * np.tanh(s / softcap)',
+        's = softcap * np.tanh(s)'),
+    'alibi sign flipped': ('bias = slopes[h] * (np.arange(skv)[None, :] - pos[:, None])',
+        'bias = slopes[h] * (pos[:, None] - np.arange(skv)[None, :])'),
+    'alibi head off by one': ('m0 ** (h + 1) if h < n',
+        'm0 ** h if h < n'),
+    'alibi second ramp': ('m1 ** (2 * (h - n) + 1)',
+        'm1 ** (h - n + 1)'),
+    'sink missing from denominator': ('l = e.sum(axis=1) + np.exp(sink - m_safe)',
+        'l = e.sum(axis=1)'),
+    'sink missing from max': ('m = np.maximum(m, sink)',
+        'm = m'),
 }
 
 
@@ -38,7 +53,7 @@ def _load_mutant(old, new):
 
 def test_unmutated_oracle_passes_battery():
     import oracle
-    for check in ALL_CHECKS:
+    for check in ALL_CHECKS + MOD_CHECKS:
         check(oracle)
 
 
@@ -46,7 +61,7 @@ def test_unmutated_oracle_passes_battery():
 def test_mutation_is_caught(name):
     mod = _load_mutant(*MUTATIONS[name])
     caught = []
-    for check in ALL_CHECKS:
+    for check in ALL_CHECKS + MOD_CHECKS:
         try:
             check(mod)
         except (AssertionError, ValueError, IndexError, FloatingPointError):
