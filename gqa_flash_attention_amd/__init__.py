@@ -12,7 +12,7 @@ import math
 
 import torch
 
-from ._lib import FAError, check, load  # noqa: F401
+from ._lib import FAError, ScoreMods, check, load  # noqa: F401
 
 __all__ = ["prefill", "decode_paged", "decode_workspace_bytes", "combine_lse",
            "kv_append", "paged_gather", "FAError", "load"]
@@ -45,12 +45,27 @@ def _strides(t):
     return (ctypes.c_int64 * 3)(*t.stride()[:3])
 
 
+def _mods(softcap, max_bias, sinks, Hq, dev):
+    """A ScoreMods for the call (None when no modifier is on)."""
+    if not softcap and not max_bias and sinks is None:
+        return None, None
+    if sinks is not None:
+        _require(sinks, "sinks", torch.float32, dev)
+        if sinks.shape != (Hq,):
+            raise ValueError("sinks must have shape [Hq]")
+    m = ScoreMods(float(softcap or 0.0), float(max_bias or 0.0), _ptr(sinks))
+    return ctypes.byref(m), m
+
+
 def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | None = None,
-            out=None, lse=None, return_lse: bool = True):
+            out=None, lse=None, return_lse: bool = True, softcap: float = 0.0,
+            max_bias: float = 0.0, sinks=None):
     """q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16 -> (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32).
 
     q, k, v and out may be strided views (e.g. slices of one fused QKV
-    tensor); only their last dimension must be unit-stride.
+    tensor); only their last dimension must be unit-stride. softcap,
+    max_bias and sinks (device fp32 [Hq]) are the score modifiers of
+    fa_score_mods (off by default).
     """
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
@@ -68,10 +83,11 @@ def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | Non
         raise ValueError("out must have q's shape")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    mref, _keep = _mods(softcap, max_bias, sinks, Hq, dev)
     check(load().fa_prefill_strided(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                     _ptr(out), _strides(out), _ptr(lse),
                                     B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), int(window),
-                                    float(scale), _stream(dev)))
+                                    float(scale), mref, _stream(dev)))
     return out, lse
 
 
@@ -82,7 +98,8 @@ def decode_workspace_bytes(B, Sq, Hq, D, max_seq_len, kv_chunk) -> int:
 def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 16,
                  kv_chunk: int = 256, causal: bool = True, window: int = 0,
                  scale: float | None = None, workspace=None, out=None, lse=None,
-                 return_lse: bool = True):
+                 return_lse: bool = True, softcap: float = 0.0, max_bias: float = 0.0,
+                 sinks=None):
     """Split-KV decode / verify.
 
     q [B,Sq,Hq,D] bf16; with block_table (int32 [B, max_pages]) the caches are
@@ -123,11 +140,12 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
         raise ValueError("out must have q's shape")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    mref, _keep = _mods(softcap, max_bias, sinks, Hq, dev)
     check(load().fa_decode_paged_strided(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
                                          _ptr(vcache), _strides(vcache), _ptr(block_table),
                                          _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
                                          B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
-                                         int(bool(causal)), int(window), float(scale),
+                                         int(bool(causal)), int(window), float(scale), mref,
                                          _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, lse
 

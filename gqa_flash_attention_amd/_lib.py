@@ -30,14 +30,22 @@ SIGNATURES = {
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P,
                              _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "fa_prefill_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+                                _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "fa_decode_paged_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                     _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+                                     _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "fa_combine_lse": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _P]),
     "fa_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_paged_gather": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
 }
+
+
+
+class ScoreMods(ctypes.Structure):
+    """fa_score_mods: logit softcap, ALiBi max_bias, sinks (device fp32 [Hq])."""
+    _fields_ = [("logit_softcap", ctypes.c_float), ("max_bias", ctypes.c_float),
+                ("sinks", ctypes.c_void_p)]
+
 
 _lib = None
 

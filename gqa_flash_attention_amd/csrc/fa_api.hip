@@ -37,6 +37,21 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 // dense layout when it is NULL. Every stride is a non-negative multiple of 8
 // elements (each row stays 16-byte aligned) below 2^40; a K/V token stride is
 // below 2^24 (the kernels keep a tile's per-lane offsets in 32 bits).
+// Score modifiers from the caller's struct (NULL: none).
+bool get_mods(const fa_score_mods* m, float& softcap, float& max_bias, const float*& sinks) {
+  softcap = 0.f;
+  max_bias = 0.f;
+  sinks = nullptr;
+  if (m == nullptr) return true;
+  if (!std::isfinite(m->logit_softcap) || m->logit_softcap < 0.f) return false;
+  if (!std::isfinite(m->max_bias) || m->max_bias < 0.f) return false;
+  if (m->sinks != nullptr && (reinterpret_cast<uintptr_t>(m->sinks) & 3u) != 0) return false;
+  softcap = m->logit_softcap;
+  max_bias = m->max_bias;
+  sinks = m->sinks;
+  return true;
+}
+
 bool get_strides(const int64_t* st, Strides dense, bool kv, Strides& out) {
   if (st == nullptr) {
     out = dense;
@@ -66,8 +81,11 @@ const char* fa_status_string(int status) {
 int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
                        const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
                        float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
-                       int causal, int window, float scale, void* stream) {
+                       int causal, int window, float scale, const fa_score_mods* mods, void* stream) {
   if (B < 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  float softcap, max_bias;
+  const float* sinks;
+  if (!get_mods(mods, softcap, max_bias, sinks)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
@@ -84,7 +102,9 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   if ((int64_t)B * Hkv * ((rows + 127) / 32) > kMaxGrid) return FA_ERR_INVALID_ARG;
-  PrefillDesc d{q, k, v, o, lse, qs, ks, vs, os, B, Hq, Hkv, Sq, Skv, D, causal, window, scale};
+  const bool any_mod = softcap > 0.f || max_bias > 0.f || sinks != nullptr;
+  PrefillDesc d{q, k, v, o, lse, qs, ks, vs, os, B, Hq, Hkv, Sq, Skv, D, causal, window, scale,
+                any_mod, softcap, max_bias, sinks};
   return to_status(launch_prefill(d, static_cast<hipStream_t>(stream)));
 }
 
@@ -92,7 +112,7 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Sq, int Skv, int D,
                int causal, int window, float scale, void* stream) {
   return fa_prefill_strided(q, nullptr, k, nullptr, v, nullptr, o, nullptr, lse, B, Hq, Hkv, Sq, Skv, D,
-                            causal, window, scale, stream);
+                            causal, window, scale, nullptr, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
@@ -111,9 +131,12 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             void* o, const int64_t* o_stride, float* lse,
                             int B, int Sq, int Hq, int Hkv, int D,
                             int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
-                            int causal, int window, float scale,
+                            int causal, int window, float scale, const fa_score_mods* mods,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  float softcap, max_bias;
+  const float* sinks;
+  if (!get_mods(mods, softcap, max_bias, sinks)) return FA_ERR_INVALID_ARG;
   if (max_pages_per_seq < 0 || kv_chunk <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
@@ -156,11 +179,12 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
   if (max_chunks > 0) {
     SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part, qs, ks, vs,
                  B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
-                 (int)n_slots, causal, window, scale};
+                 (int)n_slots, causal, window, scale, softcap, max_bias};
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
-  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, sinks,
+                 B, Sq, Hq, D};
   return to_status(launch_combine(cd, st));
 }
 
@@ -173,7 +197,7 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
                     void* workspace, size_t workspace_bytes, void* stream) {
   return fa_decode_paged_strided(q, nullptr, kcache, nullptr, vcache, nullptr, block_table, seq_lens,
                                  o, nullptr, lse, B, Sq, Hq, Hkv, D, num_pages, page_size,
-                                 max_pages_per_seq, kv_chunk, causal, window, scale, workspace,
+                                 max_pages_per_seq, kv_chunk, causal, window, scale, nullptr, workspace,
                                  workspace_bytes, stream);
 }
 
@@ -188,7 +212,7 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
   const Strides od{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
-  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, od, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, od, nullptr, B, Sq, Hq, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
 }
 

@@ -85,7 +85,36 @@ struct AttnArgs {
   float sl2;              // scale * log2(e)
   int n_rb;               // row blocks per (b, g)
   int chunk, n_slots;     // split mode: keys per chunk, partial slots per row (chunks + 1)
+  // score modifiers (kernels instantiated with MODS): softcap > 0 maps the
+  // scaled score s to softcap * tanh(s / softcap); alibi_k0 / alibi_k1 > 0
+  // add slope_h * (key - position) with slope_h = 2^(-alibi_k0 (h + 1)) for
+  // h < alibi_n and 2^(-alibi_k1 (2 (h - alibi_n) + 1)) above; sinks
+  // (prefill only; the split path's combine adds them) is a per-query-head
+  // logit in the softmax denominator, or null.
+  float scale;            // the softmax scale (used by MODS kernels)
+  float softcap, alibi_k0, alibi_k1;
+  int alibi_n;
+  const float* sinks;
 };
+
+// Fill the score-modifier fields of the kernel arguments (host side).
+// ALiBi slopes: n = 2^floor(log2 Hq), m0 = 2^(-max_bias / n),
+// m1 = 2^(-max_bias / (2 n)); head h < n gets m0^(h + 1), the others
+// m1^(2 (h - n) + 1) -- kept as exponents k0 = max_bias / n and k1 = k0 / 2.
+inline void set_mods(AttnArgs& a, float scale, float softcap, float max_bias, const float* sinks, int Hq) {
+  a.scale = scale;
+  a.softcap = softcap > 0.f ? softcap : 0.f;
+  a.alibi_k0 = a.alibi_k1 = 0.f;
+  a.alibi_n = 1;
+  if (max_bias > 0.f) {
+    int n = 1;
+    while (n * 2 <= Hq) n *= 2;
+    a.alibi_n = n;
+    a.alibi_k0 = max_bias / (float)n;
+    a.alibi_k1 = max_bias / (2.0f * (float)n);
+  }
+  a.sinks = sinks;
+}
 
 // Spread a 1-D grid over the 8 XCDs so that logical neighbours (row blocks of
 // one (b, KV head), which read the same K/V) share an XCD and its L2.
@@ -164,7 +193,7 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
   return x;
 }
 
-template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE>
+template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, bool MODS>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
@@ -319,6 +348,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   int p = 0, wpmin = 0, wpmax = 0, qi = 0, qh = 0;
   bool row_ok = false;
   bool wave_rows = false;      // this wave holds at least one row (uniform per wave)
+  float slope = 0.f;           // ALiBi slope of this lane's query head (MODS)
   int ke = 0;                  // end (exclusive) of the keys the current tile may hold
   bf16x8 qf[NQC];
   auto set_rows = [&](int b_, int g_, int rb_, int n_keys) {
@@ -337,6 +367,12 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     qi = row_ok ? r / a.G : 0;
     qh = g_ * a.G + (row_ok ? r % a.G : 0);
     p = qi + shift;                            // absolute position of this lane's row
+    if constexpr (MODS) {
+      slope = 0.f;
+      if (a.alibi_k0 > 0.f)
+        slope = fast_exp2(qh < a.alibi_n ? -a.alibi_k0 * (float)(qh + 1)
+                                         : -a.alibi_k1 * (float)(2 * (qh - a.alibi_n) + 1));
+    }
     const int64_t qoff = (int64_t)b_ * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)qh * a.q_sh +
                          8 * hl + dh * (D / DS);
 #pragma unroll
@@ -361,7 +397,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;   // reference max of the row (raw score units)
   float l_run = 0.f;         // this lane's part of the row sum
-  const float sl2 = a.sl2;
+  // exponent factor: scores are raw q.k (scale folded in here), or with
+  // score modifiers already scaled and modified (natural units)
+  const float sl2 = MODS ? kLog2e : a.sl2;
   const float thr = kRescaleLog2 / sl2;
 
   // S^T (this wave's part of the contraction) for the tile in bk
@@ -383,6 +421,24 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // Mask the boundary tiles, update the reference max (lazily), and return
   // the exponent offset -m*c for the tile starting at key tb.
   auto prepare = [&](f32x16 (&s)[NKB], int tb) -> float {
+    if constexpr (MODS) {
+      // s -> softcap(scale * s) + slope * (key - p), before the mask
+      const float inv_cap = a.softcap > 0.f ? 1.0f / a.softcap : 0.f;
+      const float pb = (float)(tb + 4 * hl - p);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          float v = s[kb][x] * a.scale;
+          if (a.softcap > 0.f) {
+            // tanh y = 1 - 2 / (1 + e^(2y)), finite for every y
+            const float e2 = fast_exp2(2.0f * kLog2e * v * inv_cap);
+            v = a.softcap * (1.0f - 2.0f * fast_rcp(1.0f + e2));
+          }
+          const int rel = 32 * kb + 8 * (x >> 2) + (x & 3);
+          s[kb][x] = fmaf(slope, pb + (float)rel, v);
+        }
+    }
     const bool full = (tb + BN <= ke) && (!a.causal || tb + BN - 1 <= wpmin) &&
                       (!a.causal || a.window <= 0 || wpmax - tb < a.window);
     if (!full) {
@@ -984,8 +1040,22 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const float l_tot = pair_sum(l_run);
     if (!row_ok) return;
     const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : fast_rcp(l_tot);
-    const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
+    float inv = empty ? 0.f : fast_rcp(l_tot);
+    float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
+    if constexpr (MODS) {
+      if (a.sinks != nullptr) {
+        // the head's sink logit joins the denominator: LSE' = logaddexp(LSE,
+        // sink), O' = O exp(LSE - LSE')
+        const float sk = a.sinks[qh];
+        const float mx = fmaxf(lse_v, sk);
+        if (mx != -INFINITY) {
+          const float el = empty ? 0.f : fast_exp2((lse_v - mx) * kLog2e);
+          const float tot = el + fast_exp2((sk - mx) * kLog2e);
+          inv *= el / tot;
+          lse_v = mx + fast_log2(tot) * kLn2;
+        }
+      }
+    }
     uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)qh * a.o_sh;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

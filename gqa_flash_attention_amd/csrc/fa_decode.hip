@@ -73,22 +73,25 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   a.B = d.B; a.Sq = d.Sq; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.Hq / d.Hkv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
+  set_mods(a, d.scale, d.softcap, d.max_bias, nullptr, d.Hq);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   a.chunk = d.kv_chunk;
   a.n_slots = d.n_slots;
-  auto kp = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE>;
-  auto kd = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE>;
-  // both kernels reserve the same LDS, so they split the work identically
+  auto kp = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, false>;
+  auto kd = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, false>;
+  auto kpm = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, true>;
+  auto kdm = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, true>;
+  // all four reserve the same LDS, so they split the work identically (the
+  // grid is sized from the plain kernels)
   static int cache_p[16], cache_d[16];
   const int resident = d.table != nullptr ? resident_workgroups(kp, NW * 64, cache_p)
                                           : resident_workgroups(kd, NW * 64, cache_d);
   // whole sets of Hkv workgroups, one per KV head
   const int grid = std::max(resident / d.Hkv, 1) * d.Hkv;
-  if (d.table != nullptr)
-    hipLaunchKernelGGL(kp, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(kd, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+  const bool mods = d.softcap > 0.f || d.max_bias > 0.f;   // sinks are added by the combine
+  auto k = d.table != nullptr ? (mods ? kpm : kp) : (mods ? kdm : kd);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -116,6 +119,7 @@ struct CombineArgs {
   uint16_t* o;
   float* lse;
   int64_t o_sb, o_ss, o_sh;     // element strides of o (sequence, row, head)
+  const float* sinks;           // per query head logit joining the denominator, or null
   int B, Sq, Hq;
 };
 
@@ -181,6 +185,9 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
     m = fmaxf(m, fmaxf(fmaxf(lw[0], lw[1]), fmaxf(lw[2], lw[3])));
   }
   m = wave_max(m);
+  // a sink logit is one more partial with O = 0
+  const float sink = c.sinks != nullptr ? c.sinks[h] : -INFINITY;
+  m = fmaxf(m, sink);
 
   const int co = CPI > 1 ? lane / SL : 0;         // partial offset of this lane in a step
   const int sl = CPI > 1 ? lane % SL : lane;      // first slice of this lane
@@ -230,6 +237,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
       __syncthreads();                            // the list is rewritten by the next block
     }
     tot = wave_sum(tot);
+    if (sink != -INFINITY) tot += fast_exp2((sink - m) * kLog2e);
     const float inv = 1.0f / tot;
     lse_out = m + fast_log2(tot) * kLn2;
 #pragma unroll
@@ -256,7 +264,8 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
 template <int D>
 hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
   CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.n_slots,
-                static_cast<uint16_t*>(d.o), d.lse, d.os.outer, d.os.token, d.os.head, d.B, d.Sq, d.Hq};
+                static_cast<uint16_t*>(d.o), d.lse, d.os.outer, d.os.token, d.os.head, d.sinks,
+                d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0, stream, c);

@@ -17,6 +17,9 @@ struct PrefillDesc {
   Strides qs, ks, vs, os;
   int B, Hq, Hkv, Sq, Skv, D, causal, window;
   float scale;
+  bool mods;                          // any score modifier below is on
+  float softcap, max_bias;            // 0 = off
+  const float* sinks;                 // device [Hq] or null
 };
 
 struct SplitDesc {
@@ -26,6 +29,7 @@ struct SplitDesc {
   Strides qs, ks, vs;
   int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, n_slots, causal, window;
   float scale;
+  float softcap, max_bias;            // 0 = off (sinks are the combine's)
 };
 
 struct CombineDesc {
@@ -35,6 +39,7 @@ struct CombineDesc {
   int kv_chunk, n_slots;     // n_slots: slots per row in memory
   void* o; float* lse;
   Strides os;                // o [B, Sq, Hq, D]
+  const float* sinks;        // device [Hq] logits joining each row's denominator, or null
   int B, Sq, Hq, D;
 };
 

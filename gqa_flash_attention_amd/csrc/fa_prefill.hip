@@ -35,12 +35,17 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   a.skv = d.Skv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
+  set_mods(a, d.scale, d.softcap, d.max_bias, d.sinks, d.Hq);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE>), dim3((unsigned)grid),
-                     dim3(C::NW * 64), 0, stream, a);
+  if (d.mods)
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, true>), dim3((unsigned)grid),
+                       dim3(C::NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, false>), dim3((unsigned)grid),
+                       dim3(C::NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

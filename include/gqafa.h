@@ -51,6 +51,27 @@ typedef enum {
 } fa_status;
 
 /*
+ * Score modifiers (the FLASH_ATTN_EXT case parameters logit_softcap,
+ * max_bias and sinks of the llama.cpp PR 28507 test report name them; the
+ * formulas are the readings stated here). With s = scale * q . k_j for the
+ * query row at position p of query head h and key j:
+ *   logit_softcap c > 0: s -> c * tanh(s / c)   (0: off)
+ *   max_bias > 0 (ALiBi): s -> s + slope_h * (j - p), with n =
+ *     2^floor(log2 Hq), slope_h = 2^(-max_bias (h + 1) / n) for h < n and
+ *     2^(-max_bias (2 (h - n) + 1) / (2 n)) otherwise   (0: off)
+ *   sinks: device fp32 [Hq]; sink_h joins the softmax denominator with no
+ *     value: l = sum_j exp(s_j) + exp(sink_h), LSE = ln l; a row with no
+ *     visible key gets O = 0 and LSE = sink_h   (NULL: off)
+ * The softcap applies before the bias, the mask after both. Values must be
+ * finite and >= 0; sinks 4-byte aligned.
+ */
+typedef struct fa_score_mods {
+  float logit_softcap;
+  float max_bias;
+  const float* sinks;
+} fa_score_mods;
+
+/*
  * Prefill attention (many query rows per sequence).
  *
  *   q   bf16 [B, Sq, Hq, D]   contiguous
@@ -82,11 +103,12 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
  *   or the inputs. Returns FA_ERR_INVALID_ARG otherwise; the rest is as
  *   fa_prefill, and the results are bitwise those of fa_prefill on
  *   contiguous copies of the same values.
+ *   mods: host pointer to score modifiers (see fa_score_mods), NULL = none.
  */
 int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
                        const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
                        float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
-                       int causal, int window, float scale, void* stream);
+                       int causal, int window, float scale, const fa_score_mods* mods, void* stream);
 
 /*
  * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
@@ -155,7 +177,8 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
  * a contiguous one, so K and V may for example be interleaved in one
  * allocation. Each is a host array of three int64, NULL for the contiguous
  * layout, with the rules of fa_prefill_strided. The results are bitwise
- * those of fa_decode_paged on contiguous copies of the same values.
+ * those of fa_decode_paged on contiguous copies of the same values. mods:
+ * host pointer to score modifiers (see fa_score_mods), NULL = none.
  */
 int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             const void* kcache, const int64_t* k_stride,
@@ -164,7 +187,7 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             void* o, const int64_t* o_stride, float* lse,
                             int B, int Sq, int Hq, int Hkv, int D,
                             int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
-                            int causal, int window, float scale,
+                            int causal, int window, float scale, const fa_score_mods* mods,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -150,7 +150,7 @@ def _st(a, b, c):
 def test_strided_prefill_validation(lib):
     f = lib.fa_prefill_strided
     def call(qs=None, ks=None, B=0):
-        return f(P, qs, P, ks, P, None, P, None, None, B, 8, 2, 16, 16, 128, 1, 0, 0.1, None)
+        return f(P, qs, P, ks, P, None, P, None, None, B, 8, 2, 16, 16, 128, 1, 0, 0.1, None, None)
     assert call() == OK                                   # NULL strides: contiguous
     assert call(qs=_st(16 * 8 * 128, 8 * 128, 128)) == OK  # explicit dense strides
     assert call(qs=_st(16 * 8 * 128, 8 * 128, 12)) == INVALID    # head stride not a multiple of 8
@@ -163,7 +163,7 @@ def test_strided_decode_validation(lib):
     f = lib.fa_decode_paged_strided
     def call(ks=None, os_=None, B=0):
         return f(P, None, P, ks, P, None, P, P, P, os_, None, B, 1, 8, 2, 128, 64, 16, 8, 64, 1, 0,
-                 0.1, P, 1 << 30, None)
+                 0.1, None, P, 1 << 30, None)
     assert call() == OK
     assert call(ks=_st(2 * 16 * 2 * 128, 2 * 2 * 128, 128)) == OK      # K/V interleaved per slot
     assert call(ks=_st(4, 8, 8)) == INVALID
@@ -183,3 +183,15 @@ def test_kv_append_validation(lib, kw, want):
     assert lib.fa_kv_append(a["kc"], a["ks"], a["vc"], a["vs"], a["table"], a["lens"], a["kn"], a["kns"],
                             a["vn"], a["vns"], a["B"], a["Snew"], a["Hkv"], a["D"], a["num_pages"],
                             a["page_size"], a["max_pages"], None) == want
+
+
+def test_score_mods_validation(lib):
+    f = lib.fa_prefill_strided
+    def call(m):
+        return f(P, None, P, None, P, None, P, None, None, 0, 8, 2, 16, 16, 128, 1, 0, 0.1,
+                 ctypes.byref(m), None)
+    assert call(_lib.ScoreMods(30.0, 8.0, P)) == OK
+    assert call(_lib.ScoreMods(-1.0, 0.0, None)) == INVALID
+    assert call(_lib.ScoreMods(0.0, float("inf"), None)) == INVALID
+    assert call(_lib.ScoreMods(0.0, float("nan"), None)) == INVALID
+    assert call(_lib.ScoreMods(0.0, 0.0, P + 2)) == INVALID          # unaligned sinks
