@@ -52,7 +52,16 @@ logit_softcap); the formulas are readings of this build:
   O = sum_j exp(s_j) v_j / l, LSE = ln l. A row with no visible key then has
   O = 0 and LSE = sink_h.
 
-The softcap applies first, then the ALiBi bias, then the mask.
+* mask (the test report's "mask" case parameter; its layout is a reading of
+  this build): an additive tensor [B or 1, Sq, >= Skv] of per-(sequence,
+  query row, key) values, shared by every head, added to the score of key j
+  of query row i (j is the key's index in the sequence, i the row's index
+  among the Sq query rows); -inf hides a key. A leading dimension of 1 is
+  shared by every sequence. Keys at or beyond a sequence's length stay
+  hidden whatever the mask holds.
+
+The softcap applies first, then the ALiBi bias, then the additive mask, and
+last the causal / window / length visibility.
 
 Every floating-point value is widened to float64 before any arithmetic.
 """
@@ -116,12 +125,12 @@ def alibi_slopes(hq: int, max_bias: float) -> np.ndarray:
 
 
 def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float,
-                 softcap: float = 0.0, bias=None, sink: float = -np.inf):
+                 softcap: float = 0.0, bias=None, sink: float = -np.inf, mask=None):
     """Two-pass softmax attention for a block of rows of one query head.
 
     q_rows [R, D], k and v [S, D], vis [R, S] boolean; optional softcap,
-    additive bias [R, S] (ALiBi) and sink logit. Returns O [R, D] and
-    LSE [R], both float64.
+    ALiBi bias [R, S], sink logit and additive mask [R, S]. Returns O [R, D]
+    and LSE [R], both float64.
 
     Pass 1 takes the maximum over the visible scores of each row (and the
     sink); pass 2 sums exp(score - max), plus exp(sink - max), and the
@@ -132,6 +141,8 @@ def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarr
         s = softcap * np.tanh(s / softcap)
     if bias is not None:
         s = s + bias
+    if mask is not None:
+        s = s + mask
     s = np.where(vis, s, -np.inf)
     # pass 1: row maximum over visible keys and the sink (-inf when neither)
     m = np.max(s, axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
@@ -150,7 +161,7 @@ def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarr
 
 def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
                   seq_lens=None, rows=None, heads=None, batches=None, row_block: int = 512,
-                  softcap: float = 0.0, max_bias: float = 0.0, sinks=None):
+                  softcap: float = 0.0, max_bias: float = 0.0, sinks=None, mask=None):
     """Reference attention for grouped-query heads.
 
     q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D] (numpy or CPU torch, any float
@@ -159,8 +170,9 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
     and batches optionally restrict which query rows / query heads /
     sequences are computed (for sampling at large sizes); the result still
     has the full shape and the rows not computed hold NaN. softcap,
-    max_bias and sinks ([Hq] logits or None) are the score modifiers of the
-    module docstring (all off by default).
+    max_bias, sinks ([Hq] logits or None) and mask ([B or 1, Sq, >= Skv]
+    additive, or None) are the score modifiers of the module docstring (all
+    off by default).
 
     Returns O [B, Sq, Hq, D] and LSE [B, Hq, Sq] in float64.
     """
@@ -181,6 +193,10 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
 
     slopes = alibi_slopes(Hq, max_bias)
     sink_v = None if sinks is None else to_f64(sinks).reshape(-1)
+    mask_v = None if mask is None else to_f64(mask)
+    if mask_v is not None:
+        assert mask_v.ndim == 3 and mask_v.shape[0] in (1, B) and mask_v.shape[1] == Sq
+        assert mask_v.shape[2] >= Skv
     o = np.full((B, Sq, Hq, D), np.nan)
     lse = np.full((B, Hq, Sq), np.nan)
     for b in batches:
@@ -198,7 +214,10 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
                     pos = rr + (skv - Sq)            # absolute positions of the rows
                     bias = slopes[h] * (np.arange(skv)[None, :] - pos[:, None])
                 sink = -np.inf if sink_v is None else float(sink_v[h])
-                ob, lb = _attend_rows(q[b, rr, h, :], kb, vb, vis, scale, softcap, bias, sink)
+                mrows = None
+                if mask_v is not None:
+                    mrows = mask_v[b if mask_v.shape[0] > 1 else 0][rr, :skv]
+                ob, lb = _attend_rows(q[b, rr, h, :], kb, vb, vis, scale, softcap, bias, sink, mrows)
                 o[b, rr, h, :] = ob
                 lse[b, h, rr] = lb
     return o, lse
@@ -232,14 +251,15 @@ def paged_gather_ref(cache, block_table, seq_lens, page_size: int, max_len: int 
 
 def decode_paged_ref(q, kcache, vcache, block_table, seq_lens, *, page_size: int,
                      causal: bool, window: int = 0, scale: float, rows=None, heads=None,
-                     softcap: float = 0.0, max_bias: float = 0.0, sinks=None):
+                     softcap: float = 0.0, max_bias: float = 0.0, sinks=None, mask=None):
     """Reference decode / speculative verify over a paged (or contiguous) cache.
 
     q [B, Sq, Hq, D] holds the Sq newest query rows of each sequence (Sq = 1
     for plain decode). When block_table is None the caches are contiguous
     [B, Smax, Hkv, D]; otherwise they are [num_pages, page_size, Hkv, D] and
     are gathered through the table first. Row i of sequence b is at
-    position seq_lens[b] - Sq + i.
+    position seq_lens[b] - Sq + i. mask, if given, is [B or 1, Sq, M]
+    indexed by token position in the sequence, M >= every seq_lens[b].
     """
     lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
     if block_table is None:
@@ -249,9 +269,16 @@ def decode_paged_ref(q, kcache, vcache, block_table, seq_lens, *, page_size: int
         max_len = max(lens) if lens else 0
         k = paged_gather_ref(kcache, block_table, lens, page_size, max_len)
         v = paged_gather_ref(vcache, block_table, lens, page_size, max_len)
+    if mask is not None:
+        # the gathered caches hold max(lens) keys; keys past each length are hidden
+        kmax = k.shape[1]
+        mask = to_f64(mask)
+        assert mask.shape[2] >= max(lens, default=0)
+        mask = mask[:, :, :kmax] if mask.shape[2] >= kmax else \
+            np.concatenate([mask, np.zeros(mask.shape[:2] + (kmax - mask.shape[2],))], axis=2)
     return attention_ref(q, k, v, causal=causal, window=window, scale=scale,
                          seq_lens=lens, rows=rows, heads=heads, softcap=softcap,
-                         max_bias=max_bias, sinks=sinks)
+                         max_bias=max_bias, sinks=sinks, mask=mask)
 
 
 def partial_attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,

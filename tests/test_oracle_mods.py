@@ -1,5 +1,5 @@
 """Pins of the oracle's score modifiers (CPU): logit softcap, ALiBi slopes
-from max_bias, and attention sinks. Each pin is independent of the oracle's
+from max_bias, attention sinks and the additive mask tensor. Each pin is independent of the oracle's
 own formula: published slope values, hand-derived closed forms, limits,
 torch's fp64 scaled_dot_product_attention with an explicit additive bias,
 and a pure-Python brute force."""
@@ -94,7 +94,7 @@ def check_alibi_against_torch_sdpa(orc):
     assert np.allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), rtol=0, atol=1e-12)
 
 
-def _brute(q, k, v, causal, window, scale, softcap, mb, sinks):
+def _brute(q, k, v, causal, window, scale, softcap, mb, sinks, mask=None):
     """Pure-Python loops, no max subtraction: the definition written out."""
     B, Sq, Hq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Skv, Hkv = len(k[0]), len(k[0][0])
@@ -117,6 +117,10 @@ def _brute(q, k, v, causal, window, scale, softcap, mb, sinks):
                     if softcap > 0:
                         s = softcap * math.tanh(s / softcap)
                     s += slopes[h] * (jj - p)
+                    if mask is not None:
+                        s += mask[b if len(mask) > 1 else 0][i][jj]
+                    if s == -math.inf:
+                        continue
                     e = math.exp(s)
                     den += e
                     for d in range(D):
@@ -130,7 +134,7 @@ def _brute(q, k, v, causal, window, scale, softcap, mb, sinks):
 
 def check_brute_force_all_modifiers(orc):
     rng = random.Random(4)
-    for trial in range(12):
+    for trial in range(16):
         B, Sq, Skv, Hkv, G, D = 1, rng.randint(1, 4), rng.randint(1, 6), rng.randint(1, 2), rng.randint(1, 3), 3
         Hq = Hkv * G
         mk = lambda *sh: np.array([rng.gauss(0, 1) for _ in range(int(np.prod(sh)))]).reshape(sh)
@@ -140,9 +144,15 @@ def check_brute_force_all_modifiers(orc):
         softcap = rng.choice([0.0, 1.5])
         mb = rng.choice([0.0, 4.0])
         sinks = [rng.gauss(0, 1) for _ in range(Hq)] if rng.random() < 0.5 else None
+        mask = None
+        if trial % 2 == 1:
+            mask = mk(B, Sq, Skv)
+            for _ in range(2):
+                mask[0, rng.randrange(Sq), rng.randrange(Skv)] = -math.inf
         o, lse = orc.attention_ref(q, k, v, causal=causal, window=window, scale=0.6, softcap=softcap,
-                                      max_bias=mb, sinks=sinks)
-        bo, bl = _brute(q.tolist(), k.tolist(), v.tolist(), causal, window, 0.6, softcap, mb, sinks)
+                                      max_bias=mb, sinks=sinks, mask=mask)
+        bo, bl = _brute(q.tolist(), k.tolist(), v.tolist(), causal, window, 0.6, softcap, mb, sinks,
+                        None if mask is None else mask.tolist())
         for vec, (b, i, h) in bo:
             assert np.allclose(o[b, i, h], vec, rtol=1e-12, atol=1e-12), trial
         for val, (b, h, i) in bl:
@@ -162,7 +172,71 @@ def check_split_combine_with_sinks_equals_whole(orc):
     assert np.allclose(o, oc, rtol=0, atol=1e-12) and np.allclose(lse, lc, rtol=0, atol=1e-12)
 
 
-MOD_CHECKS = [check_alibi_slopes_published_values, check_sink_single_key_closed_form, check_sink_limits_and_empty_row, check_softcap_closed_forms, check_softcap_large_cap_is_plain, check_alibi_against_torch_sdpa, check_brute_force_all_modifiers, check_split_combine_with_sinks_equals_whole]
+def check_mask_hiding_keys_equals_deleting_them(orc):
+    rng = np.random.default_rng(8)
+    B, Sq, Skv, Hq, Hkv, D = 2, 4, 12, 4, 2, 8
+    q, k, v = rng.standard_normal((B, Sq, Hq, D)), rng.standard_normal((B, Skv, Hkv, D)), \
+        rng.standard_normal((B, Skv, Hkv, D))
+    mask = np.zeros((B, Sq, Skv))
+    keep = [np.r_[0:3, 7:12], np.r_[2:12]]
+    mask[0, :, 3:7] = -np.inf
+    mask[1, :, 0:2] = -np.inf
+    o, lse = orc.attention_ref(q, k, v, causal=False, scale=0.4, mask=mask)
+    for b in range(B):
+        ob, lb = orc.attention_ref(q[b:b + 1], k[b:b + 1, keep[b]], v[b:b + 1, keep[b]], causal=False, scale=0.4)
+        assert np.allclose(o[b], ob[0], rtol=0, atol=1e-13) and np.allclose(lse[b], lb[0], rtol=0, atol=1e-13)
+
+
+def check_mask_against_torch_sdpa(orc):
+    torch.manual_seed(9)
+    B, Sq, Skv, Hq, Hkv, D, scale = 2, 6, 13, 6, 2, 8, 0.3
+    q, k, v = torch.randn(B, Sq, Hq, D, dtype=torch.float64), torch.randn(B, Skv, Hkv, D, dtype=torch.float64), \
+        torch.randn(B, Skv, Hkv, D, dtype=torch.float64)
+    m = 3.0 * torch.randn(B, Sq, Skv, dtype=torch.float64)
+    m[0, 2, 4] = -math.inf
+    m[1, 5, 0:5] = -math.inf
+    o, lse = orc.attention_ref(q, k, v, causal=True, window=9, scale=scale, mask=m.numpy())
+    pos = torch.arange(Sq)[:, None] + (Skv - Sq)
+    j = torch.arange(Skv)[None, :]
+    vis = (j <= pos) & (pos - j < 9)
+    full = torch.where(vis[None], m, torch.tensor(-math.inf, dtype=torch.float64))[:, None]   # [B, 1, Sq, Skv]
+    kk = k.repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+    vv = v.repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+    qq = q.permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=full, scale=scale)
+    logits = scale * (qq @ kk.transpose(-1, -2)) + full
+    assert np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def check_mask_as_causal_and_broadcast(orc):
+    rng = np.random.default_rng(10)
+    B, Sq, Hq, Hkv, D, ps = 3, 4, 4, 2, 8, 4
+    lens = [13, 4, 9]
+    P = 12
+    table = rng.permutation(P).reshape(B, 4)
+    kc, vc = rng.standard_normal((P, ps, Hkv, D)), rng.standard_normal((P, ps, Hkv, D))
+    q = rng.standard_normal((B, Sq, Hq, D))
+    # -inf wherever the key lies after the row's position: the causal rule
+    # written as a mask, in token coordinates
+    M = 16
+    mask = np.zeros((B, Sq, M))
+    for b in range(B):
+        for i in range(Sq):
+            mask[b, i, lens[b] - Sq + i + 1:] = -np.inf
+    o1, l1 = orc.decode_paged_ref(q, kc, vc, table, lens, page_size=ps, causal=False, scale=0.5, mask=mask)
+    o2, l2 = orc.decode_paged_ref(q, kc, vc, table, lens, page_size=ps, causal=True, scale=0.5)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13) and np.allclose(l1, l2, rtol=0, atol=1e-13)
+    # one [1, Sq, M] mask shared by every sequence equals it repeated
+    shared = rng.standard_normal((1, Sq, M))
+    o3, l3 = orc.decode_paged_ref(q, kc, vc, table, lens, page_size=ps, causal=True, scale=0.5, mask=shared)
+    o4, l4 = orc.decode_paged_ref(q, kc, vc, table, lens, page_size=ps, causal=True, scale=0.5,
+                                  mask=np.repeat(shared, B, axis=0))
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+    assert not np.allclose(o3, o2)
+
+
+MOD_CHECKS = [check_alibi_slopes_published_values, check_sink_single_key_closed_form, check_sink_limits_and_empty_row, check_softcap_closed_forms, check_softcap_large_cap_is_plain, check_alibi_against_torch_sdpa, check_brute_force_all_modifiers, check_split_combine_with_sinks_equals_whole, check_mask_hiding_keys_equals_deleting_them, check_mask_against_torch_sdpa, check_mask_as_causal_and_broadcast]
 
 
 def test_alibi_slopes_published_values():
@@ -195,3 +269,15 @@ def test_brute_force_all_modifiers():
 
 def test_split_combine_with_sinks_equals_whole():
     check_split_combine_with_sinks_equals_whole(oracle)
+
+
+def test_mask_hiding_keys_equals_deleting_them():
+    check_mask_hiding_keys_equals_deleting_them(oracle)
+
+
+def test_mask_against_torch_sdpa():
+    check_mask_against_torch_sdpa(oracle)
+
+
+def test_mask_as_causal_and_broadcast():
+    check_mask_as_causal_and_broadcast(oracle)

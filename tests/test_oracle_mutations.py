@@ -39,6 +39,11 @@ MUTATIONS = {
         'l = e.sum(axis=1)'),
     'sink missing from max': ('m = np.maximum(m, sink)',
         'm = m'),
+    'mask ignored': ('        s = s + mask\n', '        s = s\n'),
+    'mask subtracted': ('        s = s + mask\n', '        s = s - mask\n'),
+    'mask of the first sequence for all': ('mask_v[b if mask_v.shape[0] > 1 else 0]', 'mask_v[0]'),
+    'mask rows reversed': ('[rr, :skv]', '[rr[::-1], :skv]'),
+    'mask keys shifted in decode': ('mask = mask[:, :, :kmax] if', 'mask = np.roll(mask, 1, axis=2)[:, :, :kmax] if'),
 }
 
 
