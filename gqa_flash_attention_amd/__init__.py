@@ -45,27 +45,38 @@ def _strides(t):
     return (ctypes.c_int64 * 3)(*t.stride()[:3])
 
 
-def _mods(softcap, max_bias, sinks, Hq, dev):
+def _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, n_keys, dev):
     """A ScoreMods for the call (None when no modifier is on)."""
-    if not softcap and not max_bias and sinks is None:
+    if not softcap and not max_bias and sinks is None and mask is None:
         return None, None
     if sinks is not None:
         _require(sinks, "sinks", torch.float32, dev)
         if sinks.shape != (Hq,):
             raise ValueError("sinks must have shape [Hq]")
-    m = ScoreMods(float(softcap or 0.0), float(max_bias or 0.0), _ptr(sinks))
+    msb = mss = 0
+    if mask is not None:
+        if mask.dtype != torch.bfloat16 or not mask.is_cuda or mask.device != dev:
+            raise TypeError("mask must be a bfloat16 tensor on the inputs' device")
+        if mask.dim() != 3 or mask.shape[0] not in (1, B) or mask.shape[1] != Sq or mask.shape[2] < n_keys:
+            raise ValueError(f"mask must be [B or 1, Sq, >= {n_keys}]")
+        if mask.stride(2) != 1:
+            raise ValueError("mask keys must be unit-stride")
+        msb = mask.stride(0) if mask.shape[0] > 1 else 0
+        mss = mask.stride(1)
+    m = ScoreMods(float(softcap or 0.0), float(max_bias or 0.0), _ptr(sinks), _ptr(mask), msb, mss)
     return ctypes.byref(m), m
 
 
 def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | None = None,
             out=None, lse=None, return_lse: bool = True, softcap: float = 0.0,
-            max_bias: float = 0.0, sinks=None):
+            max_bias: float = 0.0, sinks=None, mask=None):
     """q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16 -> (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32).
 
     q, k, v and out may be strided views (e.g. slices of one fused QKV
     tensor); only their last dimension must be unit-stride. softcap,
-    max_bias and sinks (device fp32 [Hq]) are the score modifiers of
-    fa_score_mods (off by default).
+    max_bias, sinks (device fp32 [Hq]) and mask (bf16 [B or 1, Sq, >= Skv],
+    additive, shared by the heads) are the score modifiers of fa_score_mods
+    (off by default).
     """
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
@@ -83,7 +94,7 @@ def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | Non
         raise ValueError("out must have q's shape")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    mref, _keep = _mods(softcap, max_bias, sinks, Hq, dev)
+    mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, Skv, dev)
     check(load().fa_prefill_strided(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                     _ptr(out), _strides(out), _ptr(lse),
                                     B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), int(window),
@@ -99,14 +110,16 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
                  kv_chunk: int = 256, causal: bool = True, window: int = 0,
                  scale: float | None = None, workspace=None, out=None, lse=None,
                  return_lse: bool = True, softcap: float = 0.0, max_bias: float = 0.0,
-                 sinks=None):
+                 sinks=None, mask=None):
     """Split-KV decode / verify.
 
     q [B,Sq,Hq,D] bf16; with block_table (int32 [B, max_pages]) the caches are
     [num_pages, page_size, Hkv, D]; without it they are contiguous
     [B, Smax, Hkv, D] (Smax a multiple of page_size). seq_lens int32 [B].
     q, the caches and out may be strided views with a unit-stride last
-    dimension (e.g. K and V interleaved in one allocation).
+    dimension (e.g. K and V interleaved in one allocation). The score
+    modifiers are those of prefill; a mask is [B or 1, Sq, >= max_pages *
+    page_size], indexed by token position.
     """
     B, Sq, Hq, D = q.shape
     dev = q.device
@@ -140,7 +153,7 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
         raise ValueError("out must have q's shape")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
-    mref, _keep = _mods(softcap, max_bias, sinks, Hq, dev)
+    mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, max_pages * page_size, dev)
     check(load().fa_decode_paged_strided(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
                                          _ptr(vcache), _strides(vcache), _ptr(block_table),
                                          _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),

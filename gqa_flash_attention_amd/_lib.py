@@ -42,9 +42,11 @@ SIGNATURES = {
 
 
 class ScoreMods(ctypes.Structure):
-    """fa_score_mods: logit softcap, ALiBi max_bias, sinks (device fp32 [Hq])."""
+    """fa_score_mods: logit softcap, ALiBi max_bias, sinks (device fp32 [Hq]),
+    additive bf16 mask with its sequence and row strides."""
     _fields_ = [("logit_softcap", ctypes.c_float), ("max_bias", ctypes.c_float),
-                ("sinks", ctypes.c_void_p)]
+                ("sinks", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("mask_batch_stride", ctypes.c_int64), ("mask_row_stride", ctypes.c_int64)]
 
 
 _lib = None

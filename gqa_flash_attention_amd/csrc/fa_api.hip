@@ -38,17 +38,33 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 // elements (each row stays 16-byte aligned) below 2^40; a K/V token stride is
 // below 2^24 (the kernels keep a tile's per-lane offsets in 32 bits).
 // Score modifiers from the caller's struct (NULL: none).
-bool get_mods(const fa_score_mods* m, float& softcap, float& max_bias, const float*& sinks) {
-  softcap = 0.f;
-  max_bias = 0.f;
-  sinks = nullptr;
+struct Mods {
+  float softcap = 0.f, max_bias = 0.f;
+  const float* sinks = nullptr;
+  const void* mask = nullptr;
+  int64_t mask_sb = 0, mask_ss = 0;
+};
+
+bool get_mods(const fa_score_mods* m, Mods& out) {
+  out = Mods{};
   if (m == nullptr) return true;
   if (!std::isfinite(m->logit_softcap) || m->logit_softcap < 0.f) return false;
   if (!std::isfinite(m->max_bias) || m->max_bias < 0.f) return false;
   if (m->sinks != nullptr && (reinterpret_cast<uintptr_t>(m->sinks) & 3u) != 0) return false;
-  softcap = m->logit_softcap;
-  max_bias = m->max_bias;
-  sinks = m->sinks;
+  if (m->mask != nullptr) {
+    // 8-byte vector reads of 4 keys: an 8-byte aligned base and strides in
+    // whole groups of 4 elements
+    if ((reinterpret_cast<uintptr_t>(m->mask) & 7u) != 0) return false;
+    if (m->mask_batch_stride < 0 || m->mask_row_stride < 0) return false;
+    if ((m->mask_batch_stride & 3) != 0 || (m->mask_row_stride & 3) != 0) return false;
+    if (m->mask_batch_stride >= (int64_t(1) << 40) || m->mask_row_stride >= (int64_t(1) << 40)) return false;
+  }
+  out.softcap = m->logit_softcap;
+  out.max_bias = m->max_bias;
+  out.sinks = m->sinks;
+  out.mask = m->mask;
+  out.mask_sb = m->mask_batch_stride;
+  out.mask_ss = m->mask_row_stride;
   return true;
 }
 
@@ -83,9 +99,8 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
                        float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                        int causal, int window, float scale, const fa_score_mods* mods, void* stream) {
   if (B < 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-  float softcap, max_bias;
-  const float* sinks;
-  if (!get_mods(mods, softcap, max_bias, sinks)) return FA_ERR_INVALID_ARG;
+  Mods md;
+  if (!get_mods(mods, md)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
@@ -102,9 +117,8 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   if ((int64_t)B * Hkv * ((rows + 127) / 32) > kMaxGrid) return FA_ERR_INVALID_ARG;
-  const bool any_mod = softcap > 0.f || max_bias > 0.f || sinks != nullptr;
   PrefillDesc d{q, k, v, o, lse, qs, ks, vs, os, B, Hq, Hkv, Sq, Skv, D, causal, window, scale,
-                any_mod, softcap, max_bias, sinks};
+                md.softcap, md.max_bias, md.sinks, md.mask, md.mask_sb, md.mask_ss};
   return to_status(launch_prefill(d, static_cast<hipStream_t>(stream)));
 }
 
@@ -134,9 +148,8 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             int causal, int window, float scale, const fa_score_mods* mods,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-  float softcap, max_bias;
-  const float* sinks;
-  if (!get_mods(mods, softcap, max_bias, sinks)) return FA_ERR_INVALID_ARG;
+  Mods md;
+  if (!get_mods(mods, md)) return FA_ERR_INVALID_ARG;
   if (max_pages_per_seq < 0 || kv_chunk <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
@@ -179,11 +192,12 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
   if (max_chunks > 0) {
     SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part, qs, ks, vs,
                  B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
-                 (int)n_slots, causal, window, scale, softcap, max_bias};
+                 (int)n_slots, causal, window, scale, md.softcap, md.max_bias, md.mask, md.mask_sb,
+                 md.mask_ss};
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
-  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, sinks,
+  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, md.sinks,
                  B, Sq, Hq, D};
   return to_status(launch_combine(cd, st));
 }

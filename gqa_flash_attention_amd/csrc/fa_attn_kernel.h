@@ -85,23 +85,32 @@ struct AttnArgs {
   float sl2;              // scale * log2(e)
   int n_rb;               // row blocks per (b, g)
   int chunk, n_slots;     // split mode: keys per chunk, partial slots per row (chunks + 1)
-  // score modifiers (kernels instantiated with MODS): softcap > 0 maps the
+  // score modifiers (kernels instantiated with MODS >= 1; the mask needs
+  // MODS = 2; sinks are read by every prefill kernel): softcap > 0 maps the
   // scaled score s to softcap * tanh(s / softcap); alibi_k0 / alibi_k1 > 0
   // add slope_h * (key - position) with slope_h = 2^(-alibi_k0 (h + 1)) for
   // h < alibi_n and 2^(-alibi_k1 (2 (h - alibi_n) + 1)) above; sinks
   // (prefill only; the split path's combine adds them) is a per-query-head
-  // logit in the softmax denominator, or null.
+  // logit in the softmax denominator, or null; mask (bf16, or null) adds
+  // mask[b * mask_sb + i * mask_ss + key] to the score of query row i of
+  // sequence b (every head), after the softcap and the slope term.
   float scale;            // the softmax scale (used by MODS kernels)
   float softcap, alibi_k0, alibi_k1;
   int alibi_n;
   const float* sinks;
+  const uint16_t* mask;
+  int64_t mask_sb, mask_ss;
 };
 
 // Fill the score-modifier fields of the kernel arguments (host side).
 // ALiBi slopes: n = 2^floor(log2 Hq), m0 = 2^(-max_bias / n),
 // m1 = 2^(-max_bias / (2 n)); head h < n gets m0^(h + 1), the others
 // m1^(2 (h - n) + 1) -- kept as exponents k0 = max_bias / n and k1 = k0 / 2.
-inline void set_mods(AttnArgs& a, float scale, float softcap, float max_bias, const float* sinks, int Hq) {
+inline void set_mods(AttnArgs& a, float scale, float softcap, float max_bias, const float* sinks, int Hq,
+                     const void* mask, int64_t mask_sb, int64_t mask_ss) {
+  a.mask = static_cast<const uint16_t*>(mask);
+  a.mask_sb = mask_sb;
+  a.mask_ss = mask_ss;
   a.scale = scale;
   a.softcap = softcap > 0.f ? softcap : 0.f;
   a.alibi_k0 = a.alibi_k1 = 0.f;
@@ -193,7 +202,7 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
   return x;
 }
 
-template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, bool MODS>
+template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, int MODS>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
@@ -349,6 +358,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   bool row_ok = false;
   bool wave_rows = false;      // this wave holds at least one row (uniform per wave)
   float slope = 0.f;           // ALiBi slope of this lane's query head (MODS)
+  const uint16_t* mrow = nullptr;  // this lane's mask row (MODS with a mask)
+  int mlen = 0;                // keys of the sequence (the mask is read below it)
   int ke = 0;                  // end (exclusive) of the keys the current tile may hold
   bf16x8 qf[NQC];
   auto set_rows = [&](int b_, int g_, int rb_, int n_keys) {
@@ -367,11 +378,15 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     qi = row_ok ? r / a.G : 0;
     qh = g_ * a.G + (row_ok ? r % a.G : 0);
     p = qi + shift;                            // absolute position of this lane's row
-    if constexpr (MODS) {
+    if constexpr (MODS >= 1) {
       slope = 0.f;
       if (a.alibi_k0 > 0.f)
         slope = fast_exp2(qh < a.alibi_n ? -a.alibi_k0 * (float)(qh + 1)
                                          : -a.alibi_k1 * (float)(2 * (qh - a.alibi_n) + 1));
+    }
+    if constexpr (MODS >= 2) {
+      if (a.mask != nullptr) mrow = a.mask + (int64_t)b_ * a.mask_sb + (int64_t)qi * a.mask_ss;
+      mlen = n_keys;
     }
     const int64_t qoff = (int64_t)b_ * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)qh * a.q_sh +
                          8 * hl + dh * (D / DS);
@@ -399,7 +414,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   float l_run = 0.f;         // this lane's part of the row sum
   // exponent factor: scores are raw q.k (scale folded in here), or with
   // score modifiers already scaled and modified (natural units)
-  const float sl2 = MODS ? kLog2e : a.sl2;
+  const float sl2 = MODS >= 1 ? kLog2e : a.sl2;
   const float thr = kRescaleLog2 / sl2;
 
   // S^T (this wave's part of the contraction) for the tile in bk
@@ -418,11 +433,39 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
   };
 
+  // Mask values of the tile starting at key tb (MODS with a mask): for each
+  // 8-key group r of block kb, the 4 bf16 at keys tb + 32 kb + 8 r + 4 hl ..
+  // + 3 of this lane's row (the keys its score registers hold). Issued at the
+  // start of a step, ahead of the step's tile copies, so waiting for them
+  // leaves the copies in flight. Keys at or past the sequence's end read 0.
+  u32x2 mv[NKB][4];
+  auto load_mask = [&](int tb) {
+    if constexpr (MODS >= 2) {
+      if (a.mask != nullptr) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = tb + 32 * kb + 8 * r + 4 * hl;
+            if (key + 4 <= mlen) {
+              mv[kb][r] = *reinterpret_cast<const u32x2*>(mrow + key);
+            } else {
+              uint32_t w[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) w[e] = key + e < mlen ? (uint32_t)mrow[key + e] : 0u;
+              mv[kb][r] = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+            }
+          }
+      }
+    }
+  };
+
   // Mask the boundary tiles, update the reference max (lazily), and return
   // the exponent offset -m*c for the tile starting at key tb.
   auto prepare = [&](f32x16 (&s)[NKB], int tb) -> float {
-    if constexpr (MODS) {
-      // s -> softcap(scale * s) + slope * (key - p), before the mask
+    if constexpr (MODS >= 1) {
+      // s -> softcap(scale * s) + slope * (key - p) + mask, before the
+      // causal / window / length mask
       const float inv_cap = a.softcap > 0.f ? 1.0f / a.softcap : 0.f;
       const float pb = (float)(tb + 4 * hl - p);
 #pragma unroll
@@ -436,7 +479,12 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             v = a.softcap * (1.0f - 2.0f * fast_rcp(1.0f + e2));
           }
           const int rel = 32 * kb + 8 * (x >> 2) + (x & 3);
-          s[kb][x] = fmaf(slope, pb + (float)rel, v);
+          v = fmaf(slope, pb + (float)rel, v);
+          if (MODS >= 2 && a.mask != nullptr) {
+            const uint32_t w = mv[kb][x >> 2][(x & 3) >> 1];
+            v += __uint_as_float((x & 1) ? (w & 0xffff0000u) : (w << 16));
+          }
+          s[kb][x] = v;
         }
     }
     const bool full = (tb + BN <= ke) && (!a.causal || tb + BN - 1 <= wpmin) &&
@@ -887,6 +935,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // K(t) landed (copies issued after it: V(t) and the tiles behind)
         wait_e(it + NBUF - 1 < n_loc);
         __syncthreads();
+        load_mask(tb);
         u32x4 kr[NQC][NKB];
         read_k(kbuf(u), kr);
         wait_lgkm0();
@@ -920,6 +969,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // product of tile t-1, whose V buffer is refilled next
         if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
         __syncthreads();
+        load_mask(tb);
         if (it >= 1 && it + NBUF - 1 < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf((u + NBUF - 1) % NBUF));
         ke = tile_ke(cu);
         f32x16 sc[NKB];
@@ -1011,6 +1061,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const int tb = t_start + it * BN;
       if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
       __syncthreads();
+      load_mask(tb);
       if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
       if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
       combine_partner(sc, it & 1);
@@ -1042,18 +1093,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const bool empty = !(l_tot > 0.f);
     float inv = empty ? 0.f : fast_rcp(l_tot);
     float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
-    if constexpr (MODS) {
-      if (a.sinks != nullptr) {
-        // the head's sink logit joins the denominator: LSE' = logaddexp(LSE,
-        // sink), O' = O exp(LSE - LSE')
-        const float sk = a.sinks[qh];
-        const float mx = fmaxf(lse_v, sk);
-        if (mx != -INFINITY) {
-          const float el = empty ? 0.f : fast_exp2((lse_v - mx) * kLog2e);
-          const float tot = el + fast_exp2((sk - mx) * kLog2e);
-          inv *= el / tot;
-          lse_v = mx + fast_log2(tot) * kLn2;
-        }
+    if (a.sinks != nullptr) {
+      // the head's sink logit joins the denominator: LSE' = logaddexp(LSE,
+      // sink), O' = O exp(LSE - LSE')
+      const float sk = a.sinks[qh];
+      const float mx = fmaxf(lse_v, sk);
+      if (mx != -INFINITY) {
+        const float el = empty ? 0.f : fast_exp2((lse_v - mx) * kLog2e);
+        const float tot = el + fast_exp2((sk - mx) * kLog2e);
+        inv *= el / tot;
+        lse_v = mx + fast_log2(tot) * kLn2;
       }
     }
     uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)qh * a.o_sh;

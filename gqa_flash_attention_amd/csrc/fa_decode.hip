@@ -26,6 +26,9 @@ template <int D, int NWR> struct SplitCfg {
   // waves per SIMD the registers are sized for: one-wave workgroups (four
   // per CU, held by LDS) run one wave per SIMD; two- and four-wave ones two
   static constexpr int WPE = (D <= 128 && NW > 1) ? 2 : 1;
+  // with a mask (its values stay in registers through a step) the two-wave
+  // D = 128 kernel needs more than half the register file
+  static constexpr int WPE_MASK = (D == 128 && NW == 2) ? 1 : WPE;
   // tile buffers per operand: two keep 3/4 of the ring in flight; larger
   // head dims are LDS-bound
   static constexpr int NBUF = 2;
@@ -73,24 +76,29 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   a.B = d.B; a.Sq = d.Sq; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.Hq / d.Hkv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
-  set_mods(a, d.scale, d.softcap, d.max_bias, nullptr, d.Hq);
+  set_mods(a, d.scale, d.softcap, d.max_bias, nullptr, d.Hq, d.mask, d.mask_sb, d.mask_ss);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   a.chunk = d.kv_chunk;
   a.n_slots = d.n_slots;
-  auto kp = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, false>;
-  auto kd = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, false>;
-  auto kpm = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, true>;
-  auto kdm = attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, true>;
-  // all four reserve the same LDS, so they split the work identically (the
-  // grid is sized from the plain kernels)
-  static int cache_p[16], cache_d[16];
-  const int resident = d.table != nullptr ? resident_workgroups(kp, NW * 64, cache_p)
-                                          : resident_workgroups(kd, NW * 64, cache_d);
+  // score-modifier level: 0 plain, 1 softcap / ALiBi, 2 with a mask (sinks
+  // are added by the combine)
+  const int level = d.mask != nullptr ? 2 : (d.softcap > 0.f || d.max_bias > 0.f ? 1 : 0);
+  using K = decltype(&attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 0>);
+  static const K kernels[2][3] = {
+      {attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, 0>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, 1>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE_MASK, 2>},
+      {attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 0>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 1>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 2>}};
+  const int paged = d.table != nullptr ? 1 : 0;
+  const K k = kernels[paged][level];
+  // the grid is what the chosen kernel holds resident
+  static int cache[2][3][16];
+  const int resident = resident_workgroups(k, NW * 64, cache[paged][level]);
   // whole sets of Hkv workgroups, one per KV head
   const int grid = std::max(resident / d.Hkv, 1) * d.Hkv;
-  const bool mods = d.softcap > 0.f || d.max_bias > 0.f;   // sinks are added by the combine
-  auto k = d.table != nullptr ? (mods ? kpm : kp) : (mods ? kdm : kd);
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }

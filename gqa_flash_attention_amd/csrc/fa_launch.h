@@ -17,9 +17,10 @@ struct PrefillDesc {
   Strides qs, ks, vs, os;
   int B, Hq, Hkv, Sq, Skv, D, causal, window;
   float scale;
-  bool mods;                          // any score modifier below is on
   float softcap, max_bias;            // 0 = off
   const float* sinks;                 // device [Hq] or null
+  const void* mask;                   // device bf16 additive mask or null
+  int64_t mask_sb, mask_ss;           // its sequence and query-row strides (keys unit-stride)
 };
 
 struct SplitDesc {
@@ -30,6 +31,8 @@ struct SplitDesc {
   int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, n_slots, causal, window;
   float scale;
   float softcap, max_bias;            // 0 = off (sinks are the combine's)
+  const void* mask;                   // device bf16 additive mask (token positions) or null
+  int64_t mask_sb, mask_ss;
 };
 
 struct CombineDesc {

@@ -35,16 +35,22 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   a.skv = d.Skv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
-  set_mods(a, d.scale, d.softcap, d.max_bias, d.sinks, d.Hq);
+  set_mods(a, d.scale, d.softcap, d.max_bias, d.sinks, d.Hq, d.mask, d.mask_sb, d.mask_ss);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb;
   if (grid == 0) return hipSuccess;
-  if (d.mods)
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, true>), dim3((unsigned)grid),
+  // score-modifier level: 0 plain (sinks are read in the epilogue of every
+  // level), 1 softcap / ALiBi, 2 with a mask
+  const int level = d.mask != nullptr ? 2 : (d.softcap > 0.f || d.max_bias > 0.f ? 1 : 0);
+  if (level == 2)
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 2>), dim3((unsigned)grid),
+                       dim3(C::NW * 64), 0, stream, a);
+  else if (level == 1)
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 1>), dim3((unsigned)grid),
                        dim3(C::NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 0>), dim3((unsigned)grid),
                        dim3(C::NW * 64), 0, stream, a);
   return hipGetLastError();
 }

@@ -62,13 +62,24 @@ typedef enum {
  *   sinks: device fp32 [Hq]; sink_h joins the softmax denominator with no
  *     value: l = sum_j exp(s_j) + exp(sink_h), LSE = ln l; a row with no
  *     visible key gets O = 0 and LSE = sink_h   (NULL: off)
- * The softcap applies before the bias, the mask after both. Values must be
- * finite and >= 0; sinks 4-byte aligned.
+ *   mask: device bf16, additive, shared by every head: the score of key j
+ *     for query row i of sequence b gains mask[b * mask_batch_stride +
+ *     i * mask_row_stride + j] (elements; batch stride 0 shares one mask
+ *     among the sequences). j is the key's token index: 0 .. Skv-1 in
+ *     prefill, 0 .. seq_lens[b]-1 in decode/verify; every such entry must
+ *     exist. Values finite or -inf (-inf hides the key). 8-byte aligned,
+ *     strides >= 0, multiples of 4 and below 2^40   (NULL: off)
+ * The softcap applies first, then the ALiBi term, then the mask; causal,
+ * window and length masking come last. softcap and max_bias must be finite
+ * and >= 0; sinks 4-byte aligned. Invalid fields: FA_ERR_INVALID_ARG.
  */
 typedef struct fa_score_mods {
   float logit_softcap;
   float max_bias;
   const float* sinks;
+  const void* mask;
+  int64_t mask_batch_stride;
+  int64_t mask_row_stride;
 } fa_score_mods;
 
 /*

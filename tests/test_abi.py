@@ -195,3 +195,8 @@ def test_score_mods_validation(lib):
     assert call(_lib.ScoreMods(0.0, float("inf"), None)) == INVALID
     assert call(_lib.ScoreMods(0.0, float("nan"), None)) == INVALID
     assert call(_lib.ScoreMods(0.0, 0.0, P + 2)) == INVALID          # unaligned sinks
+    assert call(_lib.ScoreMods(0.0, 0.0, None, P, 0, 4096)) == OK
+    assert call(_lib.ScoreMods(0.0, 0.0, None, P + 4, 0, 4096)) == INVALID    # mask not 8-byte aligned
+    assert call(_lib.ScoreMods(0.0, 0.0, None, P, 6, 4096)) == INVALID       # stride not a multiple of 4
+    assert call(_lib.ScoreMods(0.0, 0.0, None, P, 0, -4)) == INVALID
+    assert call(_lib.ScoreMods(0.0, 0.0, None, P, 1 << 40, 4)) == INVALID

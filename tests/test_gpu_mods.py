@@ -148,3 +148,106 @@ def test_decode_c3_shape_all_mods_sampled():
                                                  heads=heads, sinks=sk.double().numpy(), **kw)
         assert_parity(o[sl][:, :, heads], lse[sl][:, heads], o_ref[:, :, heads], lse_ref[:, heads],
                       f"C3 all mods b{b}")
+
+
+def _mask(B, Sq, n_keys, seed, width=None, hide=True):
+    """bf16 additive mask [B, Sq, width] (width a multiple of 4, >= n_keys):
+    N(0, 2) values, a band of hidden keys per sequence and one fully hidden
+    row in sequence 0."""
+    g = torch.Generator().manual_seed(seed)
+    w = width or (n_keys + 3) // 4 * 4
+    m = (2.0 * torch.randn(B, Sq, w, generator=g))
+    if hide:
+        for b in range(B):
+            lo = int(torch.randint(0, max(n_keys - 8, 1), (1,), generator=g))
+            m[b, :, lo:lo + 8] = -float("inf")
+        m[0, Sq // 2, :] = -float("inf")
+    return m.to(torch.bfloat16)
+
+
+MASK_PREFILL = [
+    # B, Sq, Skv, Hq, Hkv, D, causal, window, other modifiers, broadcast
+    (2, 130, 130, 8, 2, 128, True, 0, None, False),
+    (2, 64, 200, 8, 4, 64, False, 0, None, True),
+    (1, 100, 100, 4, 2, 256, True, 40, "all", False),
+    (1, 77, 77, 4, 2, 512, True, 0, "softcap", False),
+]
+
+
+@pytest.mark.parametrize("case", MASK_PREFILL, ids=lambda c: "B{}_S{}x{}_H{}x{}_D{}_c{}_w{}_{}_bc{}".format(*c))
+def test_prefill_mask(case):
+    B, Sq, Skv, Hq, Hkv, D, causal, window, other, bcast = case
+    print(f"prefill mask {case}", flush=True)
+    q, k, v = workloads.random_inputs(B, Sq, Skv, Hq, Hkv, D, seed=Skv + D)
+    scale = 1.0 / np.sqrt(D)
+    kw, sk = _kw(other, Hq, 3, DEV) if other else ({}, None)
+    m = _mask(1 if bcast else B, Sq, Skv, seed=Sq + D, width=(Skv + 3) // 4 * 4 + 8)
+    mdev = m.to(DEV)[:, :, 4:Skv + 4]            # a strided view: row stride = width
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window, scale=scale,
+                        mask=mdev, **kw)
+    torch.cuda.synchronize()
+    rkw = dict(kw)
+    if sk is not None:
+        rkw["sinks"] = sk.double().numpy()
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, causal=causal, window=window, scale=scale,
+                                          mask=m[:, :, 4:Skv + 4], **rkw)
+    assert_parity(o, lse, o_ref, lse_ref, f"prefill mask {case}")
+    if sk is None:
+        # the row the mask hides entirely
+        assert torch.all(o[0, Sq // 2] == 0) and torch.all(torch.isneginf(lse[0, :, Sq // 2]))
+
+
+MASK_DECODE = [
+    # B, Sq, Hq, Hkv, D, page_size, max_len, len range, chunk, other modifiers
+    (4, 1, 32, 8, 128, 16, 1024, (1, 1024), 256, None),
+    (2, 8, 64, 8, 128, 16, 1024, (8, 1024), 256, "all"),
+    (3, 4, 8, 2, 64, 0, 512, (4, 512), 64, None),
+    (2, 4, 8, 2, 256, 32, 512, (4, 512), 128, "alibi"),
+    (2, 3, 8, 4, 512, 16, 256, (3, 256), 96, None),
+]
+
+
+@pytest.mark.parametrize("case", MASK_DECODE, ids=lambda c: "B{}_Sq{}_H{}x{}_D{}_ps{}_L{}_{}_c{}_{}".format(*c))
+def test_decode_mask(case):
+    B, Sq, Hq, Hkv, D, ps, max_len, (lo, hi), chunk, other = case
+    print(f"decode mask {case}", flush=True)
+    shape = workloads.DecodeShape("mask", B=B, Sq=Sq, Hq=Hq, Hkv=Hkv, D=D, page_size=ps, max_len=max_len,
+                                  len_lo=lo, len_hi=hi, kv_chunk=chunk, seed=B * 17 + D + Sq)
+    di = workloads.decode_inputs(shape, poison_tail=True)
+    kw, sk = _kw(other, Hq, 9, DEV) if other else ({}, None)
+    m = _mask(B, Sq, max_len, seed=D + Sq, hide=False)
+    m[:, :, 5:9] = -float("inf")                 # a band of hidden tokens in every row
+    table = None if di.block_table is None else di.block_table.to(DEV)
+    o, lse = fa.decode_paged(di.q.to(DEV), di.kcache.to(DEV), di.vcache.to(DEV), table, di.seq_lens.to(DEV),
+                             page_size=ps or 16, kv_chunk=chunk, causal=True, scale=shape.scale,
+                             mask=m.to(DEV), **kw)
+    torch.cuda.synchronize()
+    rkw = dict(kw)
+    if sk is not None:
+        rkw["sinks"] = sk.double().numpy()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, di.kcache, di.vcache, di.block_table, di.seq_lens,
+                                             page_size=ps or 16, causal=True, scale=shape.scale, mask=m,
+                                             **rkw)
+    assert_parity(o, lse, o_ref, lse_ref, f"decode mask {case}")
+
+
+def test_verify_mask_as_causal():
+    """The causal rule written as a mask (in token positions) with causal
+    off matches causal on, both against the oracle."""
+    shape = workloads.DecodeShape("maskc", B=3, Sq=8, Hq=32, Hkv=4, D=128, page_size=16, max_len=768,
+                                  len_lo=8, len_hi=768, kv_chunk=256, seed=123)
+    di = workloads.decode_inputs(shape)
+    lens = di.seq_lens
+    m = torch.zeros(shape.B, shape.Sq, shape.max_len)
+    for b in range(shape.B):
+        for i in range(shape.Sq):
+            m[b, i, int(lens[b]) - shape.Sq + i + 1:] = -float("inf")
+    m = m.to(torch.bfloat16)
+    args = (di.q.to(DEV), di.kcache.to(DEV), di.vcache.to(DEV), di.block_table.to(DEV), lens.to(DEV))
+    o1, l1 = fa.decode_paged(*args, page_size=16, kv_chunk=256, causal=False, mask=m.to(DEV))
+    o2, l2 = fa.decode_paged(*args, page_size=16, kv_chunk=256, causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, di.kcache, di.vcache, di.block_table, lens, page_size=16,
+                                             causal=True, scale=shape.scale)
+    assert_parity(o1, l1, o_ref, lse_ref, "verify causal-as-mask")
+    assert_parity(o2, l2, o_ref, lse_ref, "verify causal")
