@@ -16,6 +16,10 @@ each timed per call with the L2 / Infinity Cache flushed before the call,
 as algorithmic bytes (K and V of every visible token read once per KV head,
 plus Q, O, LSE, lengths and block table) over the call's duration.
 
+`--mods` instead prints one JSON line with the cost of each score modifier
+(logit softcap, ALiBi, sinks, an additive mask, all four) on the same three
+workloads, timed the same way.
+
 `roofline` describes the prefill kernel: achieved = algorithmic flop per
 launch / mean launch duration measured with HIP events on the launch
 stream, against the bf16 dense MFMA peak. `traffic` comes from the committed
@@ -135,15 +139,19 @@ def time_calls(torch, fn, steps, flush=None):
     return per, t_all0.elapsed_time(t_all1), wall
 
 
-def bench_prefill(torch, fa, workloads, dev, steps, warmup):
+def bench_prefill(torch, fa, workloads, dev, steps, warmup, mods=None, inputs=None):
     s = workloads.C2
-    q, k, v = workloads.prefill_inputs(s)
-    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    if inputs is None:
+        q, k, v = workloads.prefill_inputs(s)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    else:
+        q, k, v = inputs
     o = torch.empty_like(q)
     lse = torch.empty((s.B, s.Hq, s.Sq), dtype=torch.float32, device=dev)
+    mods = mods or {}
 
     def step():
-        fa.prefill(q, k, v, causal=True, scale=s.scale, out=o, lse=lse)
+        fa.prefill(q, k, v, causal=True, scale=s.scale, out=o, lse=lse, **mods)
 
     for _ in range(warmup):
         step()
@@ -156,8 +164,10 @@ def bench_prefill(torch, fa, workloads, dev, steps, warmup):
                 launch_tflops=flops / (launch_ms * 1e-3) / 1e12, wall_s=wall, inputs=(q, k, v))
 
 
-def bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush):
-    di = workloads.decode_inputs(shape)
+def bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush, mods=None, di=None):
+    if di is None:
+        di = workloads.decode_inputs(shape)
+    mods = mods or {}
     q = di.q.to(dev)
     kc, vc = di.kcache.to(dev), di.vcache.to(dev)
     table = None if di.block_table is None else di.block_table.to(dev)
@@ -172,7 +182,7 @@ def bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush):
 
     def step():
         fa.decode_paged(q, kc, vc, table, lens, page_size=ps, kv_chunk=shape.kv_chunk,
-                        causal=True, scale=shape.scale, workspace=ws, out=o, lse=lse)
+                        causal=True, scale=shape.scale, workspace=ws, out=o, lse=lse, **mods)
 
     for _ in range(warmup):
         step()
@@ -223,6 +233,46 @@ def cpu_baseline(workloads, inputs_cpu):
             "seconds": round(dt, 2)}
 
 
+def modifier_sets(torch, dev, Hq, B, Sq, n_keys):
+    """The score-modifier cases: none, each alone, all four (seeded sinks and
+    an N(0,1) bf16 mask per sequence)."""
+    g = torch.Generator("cpu").manual_seed(2024)
+    sinks = torch.randn(Hq, generator=g).to(dev)
+    mask = torch.randn(B, Sq, n_keys, generator=g).to(torch.bfloat16).to(dev)
+    return {"none": {}, "softcap 30": {"softcap": 30.0}, "alibi max_bias 8": {"max_bias": 8.0},
+            "sinks": {"sinks": sinks}, "mask": {"mask": mask},
+            "all four": {"softcap": 30.0, "max_bias": 8.0, "sinks": sinks, "mask": mask}}
+
+
+def bench_mods(torch, fa, workloads, dev, steps, warmup):
+    out = {"mode": "score modifier costs", "n_gpus": 1, "steps": steps, "warmup": warmup}
+    s = workloads.C2
+    q, k, v = workloads.prefill_inputs(s)
+    inputs = (q.to(dev), k.to(dev), v.to(dev))
+    # bring the clocks up before the first timed case
+    bench_prefill(torch, fa, workloads, dev, steps, 3 * warmup, inputs=inputs)
+    res = {}
+    for name, kw in modifier_sets(torch, dev, s.Hq, s.B, s.Sq, s.Skv).items():
+        print(f"prefill {name}", file=sys.stderr, flush=True)
+        r = bench_prefill(torch, fa, workloads, dev, steps, warmup, mods=kw, inputs=inputs)
+        res[name] = {"launch_ms_mean": round(r["launch_ms"], 4), "TFLOP/s": round(r["launch_tflops"], 1)}
+    out[s.name] = res
+    del inputs
+    torch.cuda.empty_cache()
+    flush = Flusher(torch, dev)
+    for shape in (workloads.C3, workloads.C5):
+        di = workloads.decode_inputs(shape)
+        cap = di.kcache.shape[1] if di.block_table is None else di.block_table.shape[1] * shape.page_size
+        res = {}
+        for name, kw in modifier_sets(torch, dev, shape.Hq, shape.B, shape.Sq, cap).items():
+            print(f"{shape.name} {name}", file=sys.stderr, flush=True)
+            r = bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush, mods=kw, di=di)
+            res[name] = {"ms_per_call_median": r["ms_per_call_median"], "GB/s": r["GB_s"]}
+        out[shape.name] = res
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +280,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and verify legs")
+    ap.add_argument("--mods", action="store_true",
+                    help="time the score modifiers on the three workloads instead of the headline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -259,6 +311,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    if args.mods:
+        print(json.dumps(bench_mods(torch, fa, workloads, dev, args.steps, args.warmup)), flush=True)
         return
 
     pre = bench_prefill(torch, fa, workloads, dev, args.steps, args.warmup)
