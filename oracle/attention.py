@@ -164,8 +164,8 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
                   softcap: float = 0.0, max_bias: float = 0.0, sinks=None, mask=None):
     """Reference attention for grouped-query heads.
 
-    q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D] (numpy or CPU torch, any float
-    dtype). seq_lens (optional, length B) gives the number of valid keys
+    q [B, Sq, Hq, Dk]; k [B, Skv, Hkv, Dk]; v [B, Skv, Hkv, Dv] (numpy or
+    CPU torch, any float dtype; the key and value head dims may differ). seq_lens (optional, length B) gives the number of valid keys
     Skv_b <= Skv per sequence; keys at or beyond it are ignored. rows, heads
     and batches optionally restrict which query rows / query heads /
     sequences are computed (for sampling at large sizes); the result still
@@ -174,14 +174,15 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
     additive, or None) are the score modifiers of the module docstring (all
     off by default).
 
-    Returns O [B, Sq, Hq, D] and LSE [B, Hq, Sq] in float64.
+    Returns O [B, Sq, Hq, Dv] and LSE [B, Hq, Sq] in float64.
     """
     q = to_f64(q)
     k = to_f64(k)
     v = to_f64(v)
-    B, Sq, Hq, D = q.shape
-    _, Skv, Hkv, Dk = k.shape
-    assert k.shape[0] == B and v.shape == k.shape and Dk == D
+    B, Sq, Hq, Dk = q.shape
+    _, Skv, Hkv, Dk2 = k.shape
+    Dv = v.shape[3]
+    assert k.shape[0] == B and v.shape[:3] == k.shape[:3] and Dk2 == Dk
     assert Hq % Hkv == 0
     group = Hq // Hkv
     if seq_lens is None:
@@ -197,7 +198,7 @@ def attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: float,
     if mask_v is not None:
         assert mask_v.ndim == 3 and mask_v.shape[0] in (1, B) and mask_v.shape[1] == Sq
         assert mask_v.shape[2] >= Skv
-    o = np.full((B, Sq, Hq, D), np.nan)
+    o = np.full((B, Sq, Hq, Dv), np.nan)
     lse = np.full((B, Hq, Sq), np.nan)
     for b in batches:
         skv = seq_lens[b]
@@ -294,8 +295,9 @@ def partial_attention_ref(q, k, v, *, causal: bool, window: int = 0, scale: floa
     q = to_f64(q)
     k = to_f64(k)
     v = to_f64(v)
-    B, Sq, Hq, D = q.shape
+    B, Sq, Hq, _ = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
+    D = v.shape[3]
     group = Hq // Hkv
     if seq_lens is None:
         seq_lens = [Skv] * B

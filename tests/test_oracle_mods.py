@@ -1,5 +1,6 @@
 """Pins of the oracle's score modifiers (CPU): logit softcap, ALiBi slopes
-from max_bias, attention sinks and the additive mask tensor. Each pin is independent of the oracle's
+from max_bias, attention sinks and the additive mask tensor; and of key and
+value head dims that differ (any multiple of 8 up to 512). Each pin is independent of the oracle's
 own formula: published slope values, hand-derived closed forms, limits,
 torch's fp64 scaled_dot_product_attention with an explicit additive bias,
 and a pure-Python brute force."""
@@ -236,7 +237,70 @@ def check_mask_as_causal_and_broadcast(orc):
     assert not np.allclose(o3, o2)
 
 
-MOD_CHECKS = [check_alibi_slopes_published_values, check_sink_single_key_closed_form, check_sink_limits_and_empty_row, check_softcap_closed_forms, check_softcap_large_cap_is_plain, check_alibi_against_torch_sdpa, check_brute_force_all_modifiers, check_split_combine_with_sinks_equals_whole, check_mask_hiding_keys_equals_deleting_them, check_mask_against_torch_sdpa, check_mask_as_causal_and_broadcast]
+def check_dk_dv_against_torch_sdpa(orc):
+    torch.manual_seed(11)
+    for Dk, Dv in ((72, 72), (80, 96), (192, 128), (320, 256), (40, 8)):
+        B, Sq, Skv, Hq, Hkv, scale = 2, 5, 9, 4, 2, 1.0 / math.sqrt(Dk)
+        q = torch.randn(B, Sq, Hq, Dk, dtype=torch.float64)
+        k = torch.randn(B, Skv, Hkv, Dk, dtype=torch.float64)
+        v = torch.randn(B, Skv, Hkv, Dv, dtype=torch.float64)
+        o, lse = orc.attention_ref(q, k, v, causal=True, window=7, scale=scale)
+        assert o.shape == (B, Sq, Hq, Dv)
+        pos = torch.arange(Sq)[:, None] + (Skv - Sq)
+        j = torch.arange(Skv)[None, :]
+        vis = (j <= pos) & (pos - j < 7)
+        add = torch.where(vis, torch.tensor(0.0, dtype=torch.float64), torch.tensor(-math.inf, dtype=torch.float64))
+        kk = k.repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+        vv = v.repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+        qq = q.permute(0, 2, 1, 3)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=add, scale=scale)
+        assert np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12), (Dk, Dv)
+        lref = torch.logsumexp(scale * (qq @ kk.transpose(-1, -2)) + add, dim=-1)
+        assert np.allclose(lse, lref.numpy(), rtol=0, atol=1e-12), (Dk, Dv)
+
+
+def check_dk_dv_padding_and_column_split(orc):
+    rng = np.random.default_rng(12)
+    B, Sq, Skv, Hq, Hkv, Dk, Dv = 1, 6, 10, 4, 2, 72, 80
+    q, k = rng.standard_normal((B, Sq, Hq, Dk)), rng.standard_normal((B, Skv, Hkv, Dk))
+    v = rng.standard_normal((B, Skv, Hkv, Dv))
+    o, lse = orc.attention_ref(q, k, v, causal=True, scale=0.2)
+    # zero columns appended to Q and K change no score
+    zq = np.concatenate([q, np.zeros((B, Sq, Hq, 56))], axis=3)
+    zk = np.concatenate([k, np.zeros((B, Skv, Hkv, 56))], axis=3)
+    o2, l2 = orc.attention_ref(zq, zk, v, causal=True, scale=0.2)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # the output's columns are those of V: splitting V splits O
+    oa, la = orc.attention_ref(q, k, v[..., :24], causal=True, scale=0.2)
+    ob, lb = orc.attention_ref(q, k, v[..., 24:], causal=True, scale=0.2)
+    assert np.allclose(o, np.concatenate([oa, ob], axis=3), rtol=0, atol=1e-14)
+    assert np.array_equal(la, lse) and np.array_equal(lb, lse)
+
+
+def check_dk_dv_brute_force(orc):
+    rng = random.Random(13)
+    for trial in range(6):
+        Sq, Skv, Hkv, G = rng.randint(1, 3), rng.randint(1, 5), rng.randint(1, 2), rng.randint(1, 2)
+        Dk, Dv = rng.choice([(3, 5), (8, 2), (4, 4), (2, 7)])
+        Hq = Hkv * G
+        mk = lambda *sh: np.array([rng.gauss(0, 1) for _ in range(int(np.prod(sh)))]).reshape(sh)
+        q, k, v = mk(1, Sq, Hq, Dk), mk(1, Skv, Hkv, Dk), mk(1, Skv, Hkv, Dv)
+        o, lse = orc.attention_ref(q, k, v, causal=True, scale=0.7)
+        for i in range(Sq):
+            for h in range(Hq):
+                g, p = h // G, i + Skv - Sq
+                w = [math.exp(0.7 * sum(q[0, i, h, d] * k[0, j, g, d] for d in range(Dk)))
+                     for j in range(Skv) if j <= p]
+                den = sum(w)
+                if den == 0:
+                    assert lse[0, h, i] == -np.inf and np.all(o[0, i, h] == 0)
+                    continue
+                want = [sum(w[j] * v[0, j, g, e] for j in range(len(w))) / den for e in range(Dv)]
+                assert np.allclose(o[0, i, h], want, rtol=1e-12, atol=1e-13), trial
+                assert abs(lse[0, h, i] - math.log(den)) < 1e-12, trial
+
+
+MOD_CHECKS = [check_alibi_slopes_published_values, check_sink_single_key_closed_form, check_sink_limits_and_empty_row, check_softcap_closed_forms, check_softcap_large_cap_is_plain, check_alibi_against_torch_sdpa, check_brute_force_all_modifiers, check_split_combine_with_sinks_equals_whole, check_mask_hiding_keys_equals_deleting_them, check_mask_against_torch_sdpa, check_mask_as_causal_and_broadcast, check_dk_dv_against_torch_sdpa, check_dk_dv_padding_and_column_split, check_dk_dv_brute_force]
 
 
 def test_alibi_slopes_published_values():
@@ -281,3 +345,15 @@ def test_mask_against_torch_sdpa():
 
 def test_mask_as_causal_and_broadcast():
     check_mask_as_causal_and_broadcast(oracle)
+
+
+def test_dk_dv_against_torch_sdpa():
+    check_dk_dv_against_torch_sdpa(oracle)
+
+
+def test_dk_dv_padding_and_column_split():
+    check_dk_dv_padding_and_column_split(oracle)
+
+
+def test_dk_dv_brute_force():
+    check_dk_dv_brute_force(oracle)

@@ -43,6 +43,7 @@ MUTATIONS = {
     'mask subtracted': ('        s = s + mask\n', '        s = s - mask\n'),
     'mask of the first sequence for all': ('mask_v[b if mask_v.shape[0] > 1 else 0]', 'mask_v[0]'),
     'mask rows reversed': ('[rr, :skv]', '[rr[::-1], :skv]'),
+    'value width taken from the key width': ('    Dv = v.shape[3]\n', '    Dv = q.shape[3]\n'),
     'mask keys shifted in decode': ('mask = mask[:, :, :kmax] if', 'mask = np.roll(mask, 1, axis=2)[:, :, :kmax] if'),
 }
 
