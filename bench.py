@@ -16,6 +16,10 @@ each timed per call with the L2 / Infinity Cache flushed before the call,
 as algorithmic bytes (K and V of every visible token read once per KV head,
 plus Q, O, LSE, lengths and block table) over the call's duration.
 
+`--head-dims` prints one JSON line with prefill TFLOP/s and decode GB/s at
+head dims other than 64/128/256/512 and with Dk != Dv (same shapes as the
+prefill and decode workloads otherwise).
+
 `--mods` instead prints one JSON line with the cost of each score modifier
 (logit softcap, ALiBi, sinks, an additive mask, all four) on the same three
 workloads, timed the same way.
@@ -233,6 +237,76 @@ def cpu_baseline(workloads, inputs_cpu):
             "seconds": round(dt, 2)}
 
 
+# padded head dims and Dk != Dv, with the full tile widths (128, 256, 512) as references
+HEAD_DIMS = [(80, 80), (96, 96), (128, 128), (192, 128), (192, 192), (256, 256), (320, 256), (512, 512)]
+
+
+def bench_head_dims(torch, fa, workloads, dev, steps, warmup):
+    """Prefill B=2 Hq=32 Hkv=8 S=4096 causal and decode B=16 Hq=32 Hkv=8
+    (lengths of the decode workload, contiguous cache, 256-token chunks) at
+    each (Dk, Dv) of HEAD_DIMS. Algorithmic work: 2 (Dk + Dv) flop per
+    visible pair per query head; K (Dk) and V (Dv) bytes of every visible
+    token once per KV head, plus Q, O and LSE."""
+    import numpy as np
+
+    out = {"mode": "head dims", "n_gpus": 1, "steps": steps, "warmup": warmup}
+    s = workloads.C2
+    pairs = visible_pairs(s.Sq, s.Skv, True, 0)
+    res = {}
+    for dk, dv in HEAD_DIMS:
+        print(f"prefill {dk}/{dv}", file=sys.stderr, flush=True)
+        g = torch.Generator("cpu").manual_seed(dk * 1000 + dv)
+        q = torch.randn(s.B, s.Sq, s.Hq, dk, generator=g).to(torch.bfloat16).to(dev)
+        k = torch.randn(s.B, s.Skv, s.Hkv, dk, generator=g).to(torch.bfloat16).to(dev)
+        v = torch.randn(s.B, s.Skv, s.Hkv, dv, generator=g).to(torch.bfloat16).to(dev)
+        o = torch.empty(s.B, s.Sq, s.Hq, dv, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(s.B, s.Hq, s.Sq, dtype=torch.float32, device=dev)
+
+        def step():
+            fa.prefill(q, k, v, causal=True, out=o, lse=lse)
+
+        for _ in range(warmup):
+            step()
+        per, _, _ = time_calls(torch, step, steps)
+        ms = sum(per) / len(per)
+        flops = 2 * (dk + dv) * s.Hq * s.B * pairs
+        res[f"{dk}/{dv}"] = {"launch_ms_mean": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1)}
+        del q, k, v, o, lse
+    out["prefill B2 Hq32 Hkv8 S4096 causal"] = res
+    torch.cuda.empty_cache()
+    c3 = workloads.C3
+    lens = workloads.decode_inputs(c3).seq_lens
+    flush = Flusher(torch, dev)
+    res = {}
+    for dk, dv in HEAD_DIMS:
+        print(f"decode {dk}/{dv}", file=sys.stderr, flush=True)
+        g = torch.Generator("cpu").manual_seed(dk * 1000 + dv + 1)
+        q = torch.randn(c3.B, 1, c3.Hq, dk, generator=g).to(torch.bfloat16).to(dev)
+        kc = torch.randn(c3.B, c3.max_len, c3.Hkv, dk, generator=g).to(torch.bfloat16).to(dev)
+        vc = torch.randn(c3.B, c3.max_len, c3.Hkv, dv, generator=g).to(torch.bfloat16).to(dev)
+        ld = lens.to(dev)
+        ws = torch.empty(fa.decode_workspace_bytes(c3.B, 1, c3.Hq, max(dk, dv), c3.max_len, c3.kv_chunk),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty(c3.B, 1, c3.Hq, dv, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(c3.B, c3.Hq, 1, dtype=torch.float32, device=dev)
+
+        def step():
+            fa.decode_paged(q, kc, vc, None, ld, page_size=16, kv_chunk=c3.kv_chunk, causal=True,
+                            workspace=ws, out=o, lse=lse)
+
+        for _ in range(warmup):
+            step()
+        per, _, _ = time_calls(torch, step, steps, flush=flush)
+        ms = sorted(per)[len(per) // 2]
+        nbytes = int(np.sum(lens.numpy().astype(np.int64))) * c3.Hkv * (dk + dv) * 2 + \
+            c3.B * c3.Hq * (dk + dv) * 2 + c3.B * c3.Hq * 4 + c3.B * 4
+        res[f"{dk}/{dv}"] = {"ms_per_call_median": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1)}
+        del q, kc, vc, ws, o, lse
+        torch.cuda.empty_cache()
+    out["decode B16 Hq32 Hkv8 lengths U[1024,16384] contiguous, 256-token chunks"] = res
+    return out
+
+
 def modifier_sets(torch, dev, Hq, B, Sq, n_keys):
     """The score-modifier cases: none, each alone, all four (seeded sinks and
     an N(0,1) bf16 mask per sequence)."""
@@ -280,6 +354,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and verify legs")
+    ap.add_argument("--head-dims", action="store_true",
+                    help="time prefill and decode at other head dims and Dk != Dv instead of the headline")
     ap.add_argument("--mods", action="store_true",
                     help="time the score modifiers on the three workloads instead of the headline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -311,6 +387,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    if args.head_dims:
+        print(json.dumps(bench_head_dims(torch, fa, workloads, dev, args.steps, args.warmup)), flush=True)
         return
 
     if args.mods:

@@ -70,7 +70,8 @@ def _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, n_keys, dev):
 def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | None = None,
             out=None, lse=None, return_lse: bool = True, softcap: float = 0.0,
             max_bias: float = 0.0, sinks=None, mask=None):
-    """q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16 -> (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32).
+    """q [B,Sq,Hq,Dk], k [B,Skv,Hkv,Dk], v [B,Skv,Hkv,Dv] bf16 ->
+    (o [B,Sq,Hq,Dv] bf16, lse [B,Hq,Sq] fp32); head dims multiples of 8 up to 512.
 
     q, k, v and out may be strided views (e.g. slices of one fused QKV
     tensor); only their last dimension must be unit-stride. softcap,
@@ -78,26 +79,27 @@ def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | Non
     additive, shared by the heads) are the score modifiers of fa_score_mods
     (off by default).
     """
-    B, Sq, Hq, D = q.shape
+    B, Sq, Hq, Dk = q.shape
     _, Skv, Hkv, _ = k.shape
+    Dv = v.shape[3]
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16, dev, strided=True)
-    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+    if v.shape[:3] != k.shape[:3] or k.shape[0] != B or k.shape[3] != Dk:
         raise ValueError("shape mismatch between q, k and v")
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
+        scale = 1.0 / math.sqrt(Dk)
     if out is None:
-        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((B, Sq, Hq, Dv), dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, dev, strided=True)
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
+    if out.shape != (B, Sq, Hq, Dv):
+        raise ValueError("out must be [B, Sq, Hq, Dv]")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, Skv, dev)
     check(load().fa_prefill_strided(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                     _ptr(out), _strides(out), _ptr(lse),
-                                    B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), int(window),
+                                    B, Hq, Hkv, Sq, Skv, Dk, Dv, int(bool(causal)), int(window),
                                     float(scale), mref, _stream(dev)))
     return out, lse
 
@@ -113,22 +115,24 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
                  sinks=None, mask=None):
     """Split-KV decode / verify.
 
-    q [B,Sq,Hq,D] bf16; with block_table (int32 [B, max_pages]) the caches are
-    [num_pages, page_size, Hkv, D]; without it they are contiguous
-    [B, Smax, Hkv, D] (Smax a multiple of page_size). seq_lens int32 [B].
+    q [B,Sq,Hq,Dk] bf16; with block_table (int32 [B, max_pages]) the caches are
+    [num_pages, page_size, Hkv, Dk or Dv]; without it they are contiguous
+    [B, Smax, Hkv, Dk or Dv] (Smax a multiple of page_size). seq_lens int32
+    [B]. Returns o [B,Sq,Hq,Dv] and lse [B,Hq,Sq].
     q, the caches and out may be strided views with a unit-stride last
     dimension (e.g. K and V interleaved in one allocation). The score
     modifiers are those of prefill; a mask is [B or 1, Sq, >= max_pages *
     page_size], indexed by token position.
     """
-    B, Sq, Hq, D = q.shape
+    B, Sq, Hq, Dk = q.shape
     dev = q.device
     _require(q, "q", torch.bfloat16, dev, strided=True)
     _require(kcache, "kcache", torch.bfloat16, dev, strided=True)
     _require(vcache, "vcache", torch.bfloat16, dev, strided=True)
     _require(seq_lens, "seq_lens", torch.int32, dev)
-    if vcache.shape != kcache.shape:
-        raise ValueError("kcache and vcache differ in shape")
+    Dv = vcache.shape[3]
+    if vcache.shape[:3] != kcache.shape[:3] or kcache.shape[3] != Dk:
+        raise ValueError("kcache / vcache shapes do not match q")
     Hkv = kcache.shape[2]
     if block_table is not None:
         _require(block_table, "block_table", torch.int32, dev)
@@ -142,22 +146,22 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
             raise ValueError("contiguous cache length must be a multiple of page_size")
         max_pages = kcache.shape[1] // page_size
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    need = decode_workspace_bytes(B, Sq, Hq, D, max_pages * page_size, kv_chunk)
+        scale = 1.0 / math.sqrt(Dk)
+    need = decode_workspace_bytes(B, Sq, Hq, max(Dk, Dv), max_pages * page_size, kv_chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
-        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((B, Sq, Hq, Dv), dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, dev, strided=True)
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
+    if out.shape != (B, Sq, Hq, Dv):
+        raise ValueError("out must be [B, Sq, Hq, Dv]")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, max_pages * page_size, dev)
     check(load().fa_decode_paged_strided(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
                                          _ptr(vcache), _strides(vcache), _ptr(block_table),
                                          _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
-                                         B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
+                                         B, Sq, Hq, Hkv, Dk, Dv, num_pages, page_size, max_pages, kv_chunk,
                                          int(bool(causal)), int(window), float(scale), mref,
                                          _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, lse
@@ -188,12 +192,14 @@ def kv_append(kcache, vcache, block_table, seq_lens, knew, vnew, *, page_size: i
     Hkv, D], else contiguous [B, Smax, Hkv, D]. Every tensor may be a strided
     view with a unit-stride last dimension.
     """
-    B, Snew, Hkv, D = knew.shape
+    B, Snew, Hkv, Dk = knew.shape
+    Dv = vnew.shape[3]
     dev = knew.device
     for t, n in ((kcache, "kcache"), (vcache, "vcache"), (knew, "knew"), (vnew, "vnew")):
         _require(t, n, torch.bfloat16, dev, strided=True)
     _require(seq_lens, "seq_lens", torch.int32, dev)
-    if vnew.shape != knew.shape or vcache.shape != kcache.shape or kcache.shape[2:] != (Hkv, D):
+    if (vnew.shape[:3] != knew.shape[:3] or vcache.shape[:3] != kcache.shape[:3]
+            or kcache.shape[2:] != (Hkv, Dk) or vcache.shape[3] != Dv):
         raise ValueError("shape mismatch between caches and new rows")
     if block_table is not None:
         _require(block_table, "block_table", torch.int32, dev)
@@ -206,7 +212,7 @@ def kv_append(kcache, vcache, block_table, seq_lens, knew, vnew, *, page_size: i
         num_pages, max_pages = 0, kcache.shape[1] // page_size
     check(load().fa_kv_append(_ptr(kcache), _strides(kcache), _ptr(vcache), _strides(vcache),
                               _ptr(block_table), _ptr(seq_lens), _ptr(knew), _strides(knew),
-                              _ptr(vnew), _strides(vnew), B, Snew, Hkv, D, num_pages, page_size,
+                              _ptr(vnew), _strides(vnew), B, Snew, Hkv, Dk, Dv, num_pages, page_size,
                               max_pages, _stream(dev)))
 
 

@@ -12,7 +12,19 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+// Tile widths the kernels are built for; partials of the split path have one
+// of these widths.
+bool tile_dim_ok(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+
+// Head dims: multiples of 8 (16-byte rows) from 8 to 512.
+bool head_dim_ok(int D) { return D >= 8 && D <= 512 && D % 8 == 0; }
+
+// The tile width that runs key / value head dims dk and dv: the smallest of
+// 64, 128, 256, 512 that holds both.
+int tile_dim(int dk, int dv) {
+  const int m = dk > dv ? dk : dv;
+  return m <= 64 ? 64 : (m <= 128 ? 128 : (m <= 256 ? 256 : 512));
+}
 
 int log2_exact(int x) {
   if (x <= 0 || (x & (x - 1)) != 0) return -1;
@@ -87,7 +99,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
-    case FA_ERR_UNSUPPORTED: return "unsupported shape (head dim must be 64, 128, 256 or 512; page size a power of two)";
+    case FA_ERR_UNSUPPORTED: return "unsupported shape (head dims must be multiples of 8 up to 512; page size a power of two)";
     case FA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
@@ -96,7 +108,7 @@ const char* fa_status_string(int status) {
 
 int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
                        const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
-                       float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                       float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int Dk, int Dv,
                        int causal, int window, float scale, const fa_score_mods* mods, void* stream) {
   if (B < 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   Mods md;
@@ -104,12 +116,14 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return FA_ERR_UNSUPPORTED;
   Strides qs, ks, vs, os;
-  const Strides qd{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
-  const Strides kd{(int64_t)Skv * Hkv * D, (int64_t)Hkv * D, D};
-  if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, qd, false, os) ||
-      !get_strides(k_stride, kd, true, ks) || !get_strides(v_stride, kd, true, vs))
+  const Strides qd{(int64_t)Sq * Hq * Dk, (int64_t)Hq * Dk, Dk};
+  const Strides od{(int64_t)Sq * Hq * Dv, (int64_t)Hq * Dv, Dv};
+  const Strides kd{(int64_t)Skv * Hkv * Dk, (int64_t)Hkv * Dk, Dk};
+  const Strides vd{(int64_t)Skv * Hkv * Dv, (int64_t)Hkv * Dv, Dv};
+  if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, od, false, os) ||
+      !get_strides(k_stride, kd, true, ks) || !get_strides(v_stride, vd, true, vs))
     return FA_ERR_INVALID_ARG;
   if (B == 0 || Sq == 0) return FA_OK;
   if (!q || !o || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
@@ -117,15 +131,15 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   if ((int64_t)B * Hkv * ((rows + 127) / 32) > kMaxGrid) return FA_ERR_INVALID_ARG;
-  PrefillDesc d{q, k, v, o, lse, qs, ks, vs, os, B, Hq, Hkv, Sq, Skv, D, causal, window, scale,
-                md.softcap, md.max_bias, md.sinks, md.mask, md.mask_sb, md.mask_ss};
+  PrefillDesc d{q, k, v, o, lse, qs, ks, vs, os, B, Hq, Hkv, Sq, Skv, tile_dim(Dk, Dv), causal, window,
+                Dk, Dv, scale, md.softcap, md.max_bias, md.sinks, md.mask, md.mask_sb, md.mask_ss};
   return to_status(launch_prefill(d, static_cast<hipStream_t>(stream)));
 }
 
 int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Sq, int Skv, int D,
                int causal, int window, float scale, void* stream) {
-  return fa_prefill_strided(q, nullptr, k, nullptr, v, nullptr, o, nullptr, lse, B, Hq, Hkv, Sq, Skv, D,
+  return fa_prefill_strided(q, nullptr, k, nullptr, v, nullptr, o, nullptr, lse, B, Hq, Hkv, Sq, Skv, D, D,
                             causal, window, scale, nullptr, stream);
 }
 
@@ -133,7 +147,8 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
   if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0) return 0;
   const int64_t slots = n_chunks_for(max_seq_len, kv_chunk) + 1;
   const int64_t rows = (int64_t)B * Hq * Sq;
-  const size_t o_bytes = align256((size_t)(rows * slots * D) * sizeof(float));
+  const int64_t width = tile_dim(D, D);     // partials are as wide as the tile
+  const size_t o_bytes = align256((size_t)(rows * slots * width) * sizeof(float));
   const size_t l_bytes = align256((size_t)(rows * slots) * sizeof(float));
   return o_bytes + l_bytes;
 }
@@ -143,7 +158,7 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             const void* vcache, const int64_t* v_stride,
                             const int32_t* block_table, const int32_t* seq_lens,
                             void* o, const int64_t* o_stride, float* lse,
-                            int B, int Sq, int Hq, int Hkv, int D,
+                            int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
                             int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
                             int causal, int window, float scale, const fa_score_mods* mods,
                             void* workspace, size_t workspace_bytes, void* stream) {
@@ -154,25 +169,29 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return FA_ERR_UNSUPPORTED;
+  const int D = tile_dim(Dk, Dv);
   const int page_shift = log2_exact(page_size);
   if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
   const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
   if (max_len > INT32_MAX) return FA_ERR_INVALID_ARG;
   if (block_table != nullptr && num_pages <= 0) return FA_ERR_INVALID_ARG;
   Strides qs, ks, vs, os;
-  const Strides qd{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
-  const Strides kd = block_table != nullptr ? Strides{(int64_t)page_size * Hkv * D, (int64_t)Hkv * D, D}
-                                            : Strides{max_len * Hkv * D, (int64_t)Hkv * D, D};
-  if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, qd, false, os) ||
-      !get_strides(k_stride, kd, true, ks) || !get_strides(v_stride, kd, true, vs))
+  const Strides qd{(int64_t)Sq * Hq * Dk, (int64_t)Hq * Dk, Dk};
+  const Strides od{(int64_t)Sq * Hq * Dv, (int64_t)Hq * Dv, Dv};
+  auto cache_dense = [&](int64_t d) {
+    return block_table != nullptr ? Strides{(int64_t)page_size * Hkv * d, (int64_t)Hkv * d, d}
+                                  : Strides{max_len * Hkv * d, (int64_t)Hkv * d, d};
+  };
+  if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, od, false, os) ||
+      !get_strides(k_stride, cache_dense(Dk), true, ks) || !get_strides(v_stride, cache_dense(Dv), true, vs))
     return FA_ERR_INVALID_ARG;
   if (B == 0 || Sq == 0) return FA_OK;
   if (!q || !o || !seq_lens || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (max_len > 0 && (!kcache || !vcache || !aligned16(kcache) || !aligned16(vcache)))
     return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_decode_workspace_bytes(B, Sq, Hq, D, (int)max_len, kv_chunk);
+  const size_t need = fa_decode_workspace_bytes(B, Sq, Hq, D, (int)max_len, kv_chunk);   // D = the tile width
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return FA_ERR_WORKSPACE;
   const int64_t max_chunks = n_chunks_for(max_len, kv_chunk);
@@ -192,13 +211,13 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
   if (max_chunks > 0) {
     SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part, qs, ks, vs,
                  B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
-                 (int)n_slots, causal, window, scale, md.softcap, md.max_bias, md.mask, md.mask_sb,
+                 (int)n_slots, causal, window, Dk, Dv, scale, md.softcap, md.max_bias, md.mask, md.mask_sb,
                  md.mask_ss};
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
   CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, md.sinks,
-                 B, Sq, Hq, D};
+                 B, Sq, Hq, D, Dv};
   return to_status(launch_combine(cd, st));
 }
 
@@ -210,7 +229,7 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
                     int causal, int window, float scale,
                     void* workspace, size_t workspace_bytes, void* stream) {
   return fa_decode_paged_strided(q, nullptr, kcache, nullptr, vcache, nullptr, block_table, seq_lens,
-                                 o, nullptr, lse, B, Sq, Hq, Hkv, D, num_pages, page_size,
+                                 o, nullptr, lse, B, Sq, Hq, Hkv, D, D, num_pages, page_size,
                                  max_pages_per_seq, kv_chunk, causal, window, scale, nullptr, workspace,
                                  workspace_bytes, stream);
 }
@@ -219,42 +238,44 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
                    int max_chunks, void* o, float* lse,
                    int B, int Sq, int Hq, int D, void* stream) {
   if (B < 0 || Sq < 0 || Hq <= 0 || max_chunks < 0) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  if (!tile_dim_ok(D)) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Sq == 0) return FA_OK;
   if (!o || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (max_chunks > 0 && (!o_part || !lse_part || !aligned16(o_part))) return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
   const Strides od{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
-  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, od, nullptr, B, Sq, Hq, D};
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, od, nullptr, B, Sq, Hq, D, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
 }
 
 int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int64_t* v_stride,
                  const int32_t* block_table, const int32_t* seq_lens,
                  const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
-                 int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
-                 void* stream) {
+                 int B, int Snew, int Hkv, int Dk, int Dv, int num_pages, int page_size,
+                 int max_pages_per_seq, void* stream) {
   if (B < 0 || Snew < 0 || Hkv <= 0 || max_pages_per_seq < 0) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(D)) return FA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return FA_ERR_UNSUPPORTED;
   const int page_shift = log2_exact(page_size);
   if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
   const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
   if (max_len > INT32_MAX) return FA_ERR_INVALID_ARG;
   if (block_table != nullptr && num_pages <= 0) return FA_ERR_INVALID_ARG;
   Strides kcs, vcs, kns, vns;
-  const Strides cd = block_table != nullptr ? Strides{(int64_t)page_size * Hkv * D, (int64_t)Hkv * D, D}
-                                            : Strides{max_len * Hkv * D, (int64_t)Hkv * D, D};
-  const Strides nd{(int64_t)Snew * Hkv * D, (int64_t)Hkv * D, D};
-  if (!get_strides(k_stride, cd, false, kcs) || !get_strides(v_stride, cd, false, vcs) ||
-      !get_strides(knew_stride, nd, false, kns) || !get_strides(vnew_stride, nd, false, vns))
+  auto cache_dense = [&](int64_t d) {
+    return block_table != nullptr ? Strides{(int64_t)page_size * Hkv * d, (int64_t)Hkv * d, d}
+                                  : Strides{max_len * Hkv * d, (int64_t)Hkv * d, d};
+  };
+  auto new_dense = [&](int64_t d) { return Strides{(int64_t)Snew * Hkv * d, (int64_t)Hkv * d, d}; };
+  if (!get_strides(k_stride, cache_dense(Dk), false, kcs) || !get_strides(v_stride, cache_dense(Dv), false, vcs) ||
+      !get_strides(knew_stride, new_dense(Dk), false, kns) || !get_strides(vnew_stride, new_dense(Dv), false, vns))
     return FA_ERR_INVALID_ARG;
   if (B == 0 || Snew == 0 || max_len == 0) return FA_OK;
   if (!kcache || !vcache || !knew || !vnew || !seq_lens) return FA_ERR_INVALID_ARG;
   if (!aligned16(kcache) || !aligned16(vcache) || !aligned16(knew) || !aligned16(vnew))
     return FA_ERR_INVALID_ARG;
   AppendDesc d{kcache, vcache, knew, vnew, block_table, seq_lens, kcs, vcs, kns, vns,
-               B, Snew, Hkv, D, num_pages, page_shift, max_pages_per_seq};
+               B, Snew, Hkv, Dk, Dv, num_pages, page_shift, max_pages_per_seq};
   return to_status(launch_append(d, static_cast<hipStream_t>(stream)));
 }
 

@@ -85,8 +85,9 @@ struct AttnArgs {
   float sl2;              // scale * log2(e)
   int n_rb;               // row blocks per (b, g)
   int chunk, n_slots;     // split mode: keys per chunk, partial slots per row (chunks + 1)
-  // score modifiers (kernels instantiated with MODS >= 1; the mask needs
-  // MODS = 2; sinks are read by every prefill kernel): softcap > 0 maps the
+  // score modifiers (kernels whose MODS level includes the score transform;
+  // the mask needs a level that includes it; sinks are read by every prefill
+  // kernel): softcap > 0 maps the
   // scaled score s to softcap * tanh(s / softcap); alibi_k0 / alibi_k1 > 0
   // add slope_h * (key - position) with slope_h = 2^(-alibi_k0 (h + 1)) for
   // h < alibi_n and 2^(-alibi_k1 (2 (h - alibi_n) + 1)) above; sinks
@@ -100,6 +101,14 @@ struct AttnArgs {
   const float* sinks;
   const uint16_t* mask;
   int64_t mask_sb, mask_ss;
+  // key and value head dims when they are below the tile's D (multiples of
+  // 8): Q columns at or past dk load as 0; a K or V tile chunk past dk / dv
+  // is filled with a copy of chunk 0 of the same key row (finite data that
+  // meets only zero Q columns, or lands in O columns that are never
+  // stored); O columns at or past dv are not stored
+  // (all of this in the padded kernels, MODS levels 3 and 4, which are used
+  // exactly when dk < D or dv < D)
+  int dk, dv;
 };
 
 // Fill the score-modifier fields of the kernel arguments (host side).
@@ -207,6 +216,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
   constexpr int BM = NW * 32 / DS;
+  // MODS level: 0 plain, 1 score transform (softcap, ALiBi), 2 transform +
+  // mask, 3 plain with head dims below D, 4 transform + mask + head dims
+  // below D
+  static_assert(MODS >= 0 && MODS <= 4, "modifier level");
+  constexpr bool kXform = MODS == 1 || MODS == 2 || MODS == 4;
+  constexpr bool kMask = MODS == 2 || MODS == 4;
+  constexpr bool kPad = MODS >= 3;
   constexpr int KCH = D / 8;                  // 16-byte chunks per row
   constexpr int NSEG = BN * KCH / 64;         // 1 KiB segments per tile
   static_assert(NSEG % NW == 0, "every wave loads whole segments");
@@ -282,6 +298,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       voff[i] = seg_voff(i);
     }
   }
+  // Head dims below D: the byte distance from this lane's chunk of segment i
+  // back to chunk 0 of its key row when the chunk lies past the real K or V
+  // head dim, else 0 (recomputed at each copy of a padded call: a few integer
+  // operations). Every copy keeps its instruction count, which the copy
+  // waits count on. Only the padded kernels use it.
+  auto seg_pad = [&](int i, bool is_v) -> uint32_t {
+    const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
+    const int lc = pc ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+    return 8 * lc >= (is_v ? a.dv : a.dk) ? 16u * (uint32_t)lc : 0u;
+  };
 
   // Paged split: a window of one sequence's block-table row, clamped into
   // [0, num_pages), staged in LDS so that no tile copy waits on a table
@@ -337,6 +363,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         if (tail && row > lim) o -= 2u * (uint32_t)((row - lim) * rs);
         src = reinterpret_cast<const char*>(kv_base + (int64_t)tb * rs) + o;
       }
+      if constexpr (kPad) src -= seg_pad(i, is_v);
       dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
     }
   };
@@ -378,13 +405,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     qi = row_ok ? r / a.G : 0;
     qh = g_ * a.G + (row_ok ? r % a.G : 0);
     p = qi + shift;                            // absolute position of this lane's row
-    if constexpr (MODS >= 1) {
+    if constexpr (kXform) {
       slope = 0.f;
       if (a.alibi_k0 > 0.f)
         slope = fast_exp2(qh < a.alibi_n ? -a.alibi_k0 * (float)(qh + 1)
                                          : -a.alibi_k1 * (float)(2 * (qh - a.alibi_n) + 1));
     }
-    if constexpr (MODS >= 2) {
+    if constexpr (kMask) {
       if (a.mask != nullptr) mrow = a.mask + (int64_t)b_ * a.mask_sb + (int64_t)qi * a.mask_ss;
       mlen = n_keys;
     }
@@ -393,7 +420,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
+      const bool in_d = !kPad || 8 * hl + dh * (D / DS) + 16 * c < a.dk;
+      if (row_ok && in_d) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
       qf[c] = as_bf16x8(w);
     }
   };
@@ -414,7 +442,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   float l_run = 0.f;         // this lane's part of the row sum
   // exponent factor: scores are raw q.k (scale folded in here), or with
   // score modifiers already scaled and modified (natural units)
-  const float sl2 = MODS >= 1 ? kLog2e : a.sl2;
+  const float sl2 = kXform ? kLog2e : a.sl2;
   const float thr = kRescaleLog2 / sl2;
 
   // S^T (this wave's part of the contraction) for the tile in bk
@@ -440,7 +468,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // leaves the copies in flight. Keys at or past the sequence's end read 0.
   u32x2 mv[NKB][4];
   auto load_mask = [&](int tb) {
-    if constexpr (MODS >= 2) {
+    if constexpr (kMask) {
       if (a.mask != nullptr) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -463,7 +491,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // Mask the boundary tiles, update the reference max (lazily), and return
   // the exponent offset -m*c for the tile starting at key tb.
   auto prepare = [&](f32x16 (&s)[NKB], int tb) -> float {
-    if constexpr (MODS >= 1) {
+    if constexpr (kXform) {
       // s -> softcap(scale * s) + slope * (key - p) + mask, before the
       // causal / window / length mask
       const float inv_cap = a.softcap > 0.f ? 1.0f / a.softcap : 0.f;
@@ -480,7 +508,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           }
           const int rel = 32 * kb + 8 * (x >> 2) + (x & 3);
           v = fmaf(slope, pb + (float)rel, v);
-          if (MODS >= 2 && a.mask != nullptr) {
+          if (kMask && a.mask != nullptr) {
             const uint32_t w = mv[kb][x >> 2][(x & 3) >> 1];
             v += __uint_as_float((x & 1) ? (w & 0xffff0000u) : (w << 16));
           }
@@ -1113,7 +1141,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
         u32x2 val = {pack_bf16(oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv),
                      pack_bf16(oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv)};
-        *reinterpret_cast<u32x2*>(dst + d0) = val;
+        if (!kPad || d0 < a.dv) *reinterpret_cast<u32x2*>(dst + d0) = val;
       }
     if (a.lse != nullptr && hl == 0 && dh == 0) a.lse[((int64_t)b * a.Hq + qh) * a.Sq + qi] = lse_v;
   }

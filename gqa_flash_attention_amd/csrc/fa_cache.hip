@@ -3,6 +3,8 @@
 // decode or verify call over the same cache. All operands are read and
 // written by stride (ATOM PR 2938, Summary: only the innermost dimension
 // needs unit stride), so K and V may share one allocation.
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -19,15 +21,16 @@ struct AppendArgs {
   const int32_t* seq_lens;    // [B]: tokens in the cache including the new rows
   int64_t kc_sb, kc_ss, kc_sh, vc_sb, vc_ss, vc_sh;   // cache strides (page or sequence, slot, head)
   int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;   // new rows [B, Snew, Hkv, D]
-  int B, Snew, Hkv, D, num_pages, page_shift, max_pages;
+  int B, Snew, Hkv, dk, dv, num_pages, page_shift, max_pages;
 };
 
-// One thread per 16-byte chunk of the new rows; grid-stride. New row i of
-// sequence b lands at token seq_lens[b] - Snew + i. Rows whose token would be
-// negative (a sequence shorter than Snew) and rows whose block-table entry is
-// outside [0, num_pages) are not written.
+// One thread per 16-byte chunk of the new rows (the wider of the K and V
+// rows); grid-stride. New row i of sequence b lands at token seq_lens[b] -
+// Snew + i. Rows whose token would be negative (a sequence shorter than
+// Snew) and rows whose block-table entry is outside [0, num_pages) are not
+// written.
 __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
-  const int chunks = a.D / 8;
+  const int chunks = max(a.dk, a.dv) / 8;
   const int64_t total = (int64_t)a.B * a.Snew * a.Hkv * chunks;
   const int64_t cap = (int64_t)a.max_pages << a.page_shift;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
@@ -54,12 +57,16 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
       vrow = (int64_t)b * a.vc_sb + t * a.vc_ss;
     }
     const int64_t e = 8 * ch;
-    const u32x4 kw = *reinterpret_cast<const u32x4*>(a.kn + (int64_t)b * a.kn_sb + (int64_t)i * a.kn_ss +
-                                                     (int64_t)g * a.kn_sh + e);
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(a.vn + (int64_t)b * a.vn_sb + (int64_t)i * a.vn_ss +
-                                                     (int64_t)g * a.vn_sh + e);
-    *reinterpret_cast<u32x4*>(a.kc + krow + (int64_t)g * a.kc_sh + e) = kw;
-    *reinterpret_cast<u32x4*>(a.vc + vrow + (int64_t)g * a.vc_sh + e) = vw;
+    if (e < a.dk) {
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(a.kn + (int64_t)b * a.kn_sb + (int64_t)i * a.kn_ss +
+                                                       (int64_t)g * a.kn_sh + e);
+      *reinterpret_cast<u32x4*>(a.kc + krow + (int64_t)g * a.kc_sh + e) = kw;
+    }
+    if (e < a.dv) {
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(a.vn + (int64_t)b * a.vn_sb + (int64_t)i * a.vn_ss +
+                                                       (int64_t)g * a.vn_sh + e);
+      *reinterpret_cast<u32x4*>(a.vc + vrow + (int64_t)g * a.vc_sh + e) = vw;
+    }
   }
 }
 
@@ -71,8 +78,8 @@ hipError_t launch_append(const AppendDesc& d, hipStream_t stream) {
                d.table, d.seq_lens,
                d.kcs.outer, d.kcs.token, d.kcs.head, d.vcs.outer, d.vcs.token, d.vcs.head,
                d.kns.outer, d.kns.token, d.kns.head, d.vns.outer, d.vns.token, d.vns.head,
-               d.B, d.Snew, d.Hkv, d.D, d.num_pages, d.page_shift, d.max_pages};
-  const int64_t total = (int64_t)d.B * d.Snew * d.Hkv * (d.D / 8);
+               d.B, d.Snew, d.Hkv, d.dk, d.dv, d.num_pages, d.page_shift, d.max_pages};
+  const int64_t total = (int64_t)d.B * d.Snew * d.Hkv * (std::max(d.dk, d.dv) / 8);
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;

@@ -26,9 +26,10 @@ template <int D, int NWR> struct SplitCfg {
   // waves per SIMD the registers are sized for: one-wave workgroups (four
   // per CU, held by LDS) run one wave per SIMD; two- and four-wave ones two
   static constexpr int WPE = (D <= 128 && NW > 1) ? 2 : 1;
-  // with a mask (its values stay in registers through a step) the two-wave
-  // D = 128 kernel needs more than half the register file
-  static constexpr int WPE_MASK = (D == 128 && NW == 2) ? 1 : WPE;
+  // with a mask (its values stay in registers through a step) or head dims
+  // below D, the two- and four-wave D = 128 kernels need more than half the
+  // register file
+  static constexpr int WPE_MASK = (D == 128 && NW >= 2) ? 1 : WPE;
   // tile buffers per operand: two keep 3/4 of the ring in flight; larger
   // head dims are LDS-bound
   static constexpr int NBUF = 2;
@@ -76,26 +77,35 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   a.B = d.B; a.Sq = d.Sq; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.Hq / d.Hkv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
+  a.dk = d.dk;
+  a.dv = d.dv;
   set_mods(a, d.scale, d.softcap, d.max_bias, nullptr, d.Hq, d.mask, d.mask_sb, d.mask_ss);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   a.chunk = d.kv_chunk;
   a.n_slots = d.n_slots;
-  // score-modifier level: 0 plain, 1 softcap / ALiBi, 2 with a mask (sinks
-  // are added by the combine)
-  const int level = d.mask != nullptr ? 2 : (d.softcap > 0.f || d.max_bias > 0.f ? 1 : 0);
+  // kernel level: 0 plain, 1 softcap / ALiBi, 2 with a mask; with head dims
+  // below D, 3 (no score transform) or 4 (transform and mask). Sinks are
+  // added by the combine.
+  const bool xform = d.softcap > 0.f || d.max_bias > 0.f;
+  const int level = (d.dk < D || d.dv < D) ? (xform || d.mask != nullptr ? 4 : 3)
+                    : d.mask != nullptr ? 2 : (xform ? 1 : 0);
   using K = decltype(&attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 0>);
-  static const K kernels[2][3] = {
+  static const K kernels[2][5] = {
       {attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, 0>,
        attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, 1>,
-       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE_MASK, 2>},
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE_MASK, 2>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE_MASK, 3>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE_MASK, 4>},
       {attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 0>,
        attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 1>,
-       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 2>}};
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 2>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 3>,
+       attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 4>}};
   const int paged = d.table != nullptr ? 1 : 0;
   const K k = kernels[paged][level];
   // the grid is what the chosen kernel holds resident
-  static int cache[2][3][16];
+  static int cache[2][5][16];
   const int resident = resident_workgroups(k, NW * 64, cache[paged][level]);
   // whole sets of Hkv workgroups, one per KV head
   const int grid = std::max(resident / d.Hkv, 1) * d.Hkv;
@@ -128,6 +138,7 @@ struct CombineArgs {
   float* lse;
   int64_t o_sb, o_ss, o_sh;     // element strides of o (sequence, row, head)
   const float* sinks;           // per query head logit joining the denominator, or null
+  int dv;                       // columns of O written
   int B, Sq, Hq;
 };
 
@@ -263,7 +274,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
 #pragma unroll
     for (int v = 0; v < SPL; ++v) {
       u32x2 val = {pack_bf16(acc[v][0], acc[v][1]), pack_bf16(acc[v][2], acc[v][3])};
-      *reinterpret_cast<u32x2*>(dst + 4 * (sl + 64 * v)) = val;
+      if (4 * (sl + 64 * v) < c.dv) *reinterpret_cast<u32x2*>(dst + 4 * (sl + 64 * v)) = val;
     }
   }
   if (c.lse != nullptr && lane == 0) c.lse[((int64_t)b * c.Hq + h) * c.Sq + i] = lse_out;
@@ -273,7 +284,7 @@ template <int D>
 hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
   CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.n_slots,
                 static_cast<uint16_t*>(d.o), d.lse, d.os.outer, d.os.token, d.os.head, d.sinks,
-                d.B, d.Sq, d.Hq};
+                d.dv, d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0, stream, c);

@@ -15,7 +15,8 @@ struct Strides {
 struct PrefillDesc {
   const void* q; const void* k; const void* v; void* o; float* lse;
   Strides qs, ks, vs, os;
-  int B, Hq, Hkv, Sq, Skv, D, causal, window;
+  int B, Hq, Hkv, Sq, Skv, D, causal, window;   // D: the tile width (64, 128, 256 or 512)
+  int dk, dv;                         // key / value head dims, multiples of 8, <= D
   float scale;
   float softcap, max_bias;            // 0 = off
   const float* sinks;                 // device [Hq] or null
@@ -29,6 +30,7 @@ struct SplitDesc {
   float* o_part; float* lse_part;   // [B, Hq, Sq, n_slots(, D)]: chunks + 1 slots per row
   Strides qs, ks, vs;
   int B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages, kv_chunk, n_slots, causal, window;
+  int dk, dv;                         // key / value head dims, multiples of 8, <= D
   float scale;
   float softcap, max_bias;            // 0 = off (sinks are the combine's)
   const void* mask;                   // device bf16 additive mask (token positions) or null
@@ -43,14 +45,15 @@ struct CombineDesc {
   void* o; float* lse;
   Strides os;                // o [B, Sq, Hq, D]
   const float* sinks;        // device [Hq] logits joining each row's denominator, or null
-  int B, Sq, Hq, D;
+  int B, Sq, Hq, D;          // D: width of a partial (64, 128, 256 or 512)
+  int dv;                    // columns of O written (a multiple of 8, <= D)
 };
 
 struct AppendDesc {
   void* kcache; void* vcache; const void* knew; const void* vnew;
   const int32_t* table; const int32_t* seq_lens;
   Strides kcs, vcs, kns, vns;
-  int B, Snew, Hkv, D, num_pages, page_shift, max_pages;
+  int B, Snew, Hkv, dk, dv, num_pages, page_shift, max_pages;   // dk, dv: multiples of 8
 };
 
 struct GatherDesc {

@@ -35,15 +35,26 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   a.skv = d.Skv;
   a.causal = d.causal; a.window = d.window;
   a.sl2 = d.scale * kLog2e;
+  a.dk = d.dk;
+  a.dv = d.dv;
   set_mods(a, d.scale, d.softcap, d.max_bias, d.sinks, d.Hq, d.mask, d.mask_sb, d.mask_ss);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)d.B * d.Hkv * a.n_rb;
   if (grid == 0) return hipSuccess;
-  // score-modifier level: 0 plain (sinks are read in the epilogue of every
-  // level), 1 softcap / ALiBi, 2 with a mask
-  const int level = d.mask != nullptr ? 2 : (d.softcap > 0.f || d.max_bias > 0.f ? 1 : 0);
-  if (level == 2)
+  // kernel level: 0 plain (sinks are read in the epilogue of every level),
+  // 1 softcap / ALiBi, 2 with a mask; with head dims below D, 3 (no score
+  // transform) or 4 (transform and mask)
+  const bool xform = d.softcap > 0.f || d.max_bias > 0.f;
+  const int level = (d.dk < D || d.dv < D) ? (xform || d.mask != nullptr ? 4 : 3)
+                    : d.mask != nullptr ? 2 : (xform ? 1 : 0);
+  if (level == 4)
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 4>), dim3((unsigned)grid),
+                       dim3(C::NW * 64), 0, stream, a);
+  else if (level == 3)
+    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 3>), dim3((unsigned)grid),
+                       dim3(C::NW * 64), 0, stream, a);
+  else if (level == 2)
     hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 2>), dim3((unsigned)grid),
                        dim3(C::NW * 64), 0, stream, a);
   else if (level == 1)

@@ -92,8 +92,11 @@ typedef struct fa_score_mods {
  *   lse fp32 [B, Hq, Sq]      output, may be NULL (not written)
  *
  * B, Sq, Skv >= 0 (an empty batch or Sq = 0 writes nothing; Skv = 0 gives
- * O = 0 and LSE = -inf); Hq, Hkv > 0 with Hq % Hkv == 0; D in
- * {64,128,256,512}; causal 0/1; window >= 0; scale finite and > 0.
+ * O = 0 and LSE = -inf); Hq, Hkv > 0 with Hq % Hkv == 0; D a multiple of 8
+ * in [8, 512] (FA_ERR_UNSUPPORTED otherwise); causal 0/1; window >= 0;
+ * scale finite and > 0. A head dim runs on the smallest tile of 64, 128,
+ * 256 or 512 columns that holds it; the columns past it are zeros in the
+ * tiles and never stored.
  */
 int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Sq, int Skv, int D,
@@ -115,15 +118,21 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
  *   fa_prefill, and the results are bitwise those of fa_prefill on
  *   contiguous copies of the same values.
  *   mods: host pointer to score modifiers (see fa_score_mods), NULL = none.
+ *   Dk, Dv: the key and value head dims, which may differ (each a multiple
+ *   of 8 in [8, 512]): q and k are [.., Dk], v and o [.., Dv]; the tile is
+ *   the smallest of 64, 128, 256, 512 that holds both. fa_prefill is
+ *   Dk = Dv = D.
  */
 int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
                        const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
-                       float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                       float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int Dk, int Dv,
                        int causal, int window, float scale, const fa_score_mods* mods, void* stream);
 
 /*
  * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
- * [B, Hq, Sq, n_slots, D] and their LSEs [B, Hq, Sq, n_slots], with
+ * [B, Hq, Sq, n_slots, W] and their LSEs [B, Hq, Sq, n_slots], with W the
+ * tile width for head dim D (the smallest of 64, 128, 256, 512 that holds
+ * it; with Dk != Dv pass the larger of the two), and
  * n_slots = ceil(max_seq_len / kv_chunk) + 1 (a sequence's keys meet at most
  * that many workgroup ranges of the balanced split), each region 256-byte
  * aligned. Returns 0 for invalid sizes.
@@ -189,14 +198,17 @@ int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
  * allocation. Each is a host array of three int64, NULL for the contiguous
  * layout, with the rules of fa_prefill_strided. The results are bitwise
  * those of fa_decode_paged on contiguous copies of the same values. mods:
- * host pointer to score modifiers (see fa_score_mods), NULL = none.
+ * host pointer to score modifiers (see fa_score_mods), NULL = none. Dk and
+ * Dv are the key and value head dims as in fa_prefill_strided: q and kcache
+ * are [.., Dk], vcache and o [.., Dv]; the workspace is sized with
+ * max(Dk, Dv).
  */
 int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             const void* kcache, const int64_t* k_stride,
                             const void* vcache, const int64_t* v_stride,
                             const int32_t* block_table, const int32_t* seq_lens,
                             void* o, const int64_t* o_stride, float* lse,
-                            int B, int Sq, int Hq, int Hkv, int D,
+                            int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
                             int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
                             int causal, int window, float scale, const fa_score_mods* mods,
                             void* workspace, size_t workspace_bytes, void* stream);
@@ -208,6 +220,7 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
  * Chunks with LSE_c = -inf have weight 0; a row whose chunks are all empty
  * gets O = 0, LSE = -inf.
  *
+ *   D        64, 128, 256 or 512 (the partial width of the split path)
  *   o_part   fp32 [B, Hq, Sq, max_chunks, D] (each normalised by its own sum)
  *   lse_part fp32 [B, Hq, Sq, max_chunks]
  *   n_chunks int32 [B] on the device: leading chunks of sequence b to merge
@@ -223,15 +236,17 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
  * KV-cache append: the step before a decode or verify call, which writes the
  * Snew newest K/V rows of each sequence into the cache.
  *
- *   kcache, vcache  bf16 [num_pages, page_size, Hkv, D] with block_table
+ *   kcache, vcache  bf16 [num_pages, page_size, Hkv, Dk or Dv] with block_table
  *                   (int32 [B, max_pages_per_seq]), or contiguous
  *                   [B, max_pages_per_seq * page_size, Hkv, D] when
  *                   block_table is NULL; written in place
  *   seq_lens        int32 [B] on the device: tokens in each cache AFTER the
  *                   append (the convention of fa_decode_paged); clamped to
  *                   [0, max_pages_per_seq * page_size]
- *   knew, vnew      bf16 [B, Snew, Hkv, D]: row i of sequence b goes to token
- *                   seq_lens[b] - Snew + i
+ *   knew, vnew      bf16 [B, Snew, Hkv, Dk] and [B, Snew, Hkv, Dv]: row i of
+ *                   sequence b goes to token seq_lens[b] - Snew + i; the
+ *                   caches have the same head dims (multiples of 8 in
+ *                   [8, 512])
  *   *_stride        host int64[3] element strides (outer, token, head) of the
  *                   four tensors, NULL for the contiguous layout, with the
  *                   rules of fa_prefill_strided (head dim unit-stride)
@@ -244,8 +259,8 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
 int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int64_t* v_stride,
                  const int32_t* block_table, const int32_t* seq_lens,
                  const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
-                 int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
-                 void* stream);
+                 int B, int Snew, int Hkv, int Dk, int Dv, int num_pages, int page_size,
+                 int max_pages_per_seq, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

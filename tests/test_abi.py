@@ -62,7 +62,8 @@ def _prefill(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(D=96), UNSUPPORTED), (dict(D=32), UNSUPPORTED), (dict(D=576), UNSUPPORTED),
+    (dict(D=576), UNSUPPORTED), (dict(D=84), UNSUPPORTED), (dict(D=0), UNSUPPORTED),
+    (dict(D=96, B=0), OK), (dict(D=32, B=0), OK), (dict(D=8, B=0), OK), (dict(D=72, B=0), OK),
     (dict(Hq=6, Hkv=4), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID),
     (dict(B=-1), INVALID), (dict(Sq=-1), INVALID), (dict(Skv=-2), INVALID),
     (dict(window=4, causal=0), INVALID), (dict(window=-1), INVALID), (dict(causal=2), INVALID),
@@ -88,8 +89,8 @@ def _decode(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(D=80), UNSUPPORTED), (dict(page_size=12), UNSUPPORTED), (dict(page_size=0), UNSUPPORTED),
-    (dict(page_size=1 << 17), UNSUPPORTED),
+    (dict(D=520), UNSUPPORTED), (dict(D=100), UNSUPPORTED), (dict(page_size=12), UNSUPPORTED),
+    (dict(page_size=0), UNSUPPORTED), (dict(page_size=1 << 17), UNSUPPORTED), (dict(D=80, B=0), OK),
     (dict(Hq=7), INVALID), (dict(chunk=0), INVALID), (dict(max_pages=-1), INVALID),
     (dict(window=3, causal=0), INVALID), (dict(scale=0.0), INVALID),
     (dict(num_pages=0), INVALID), (dict(lens=None), INVALID), (dict(q=None), INVALID),
@@ -106,8 +107,11 @@ def test_workspace_bytes(lib):
     f = lib.fa_decode_workspace_bytes
     # C3 shape: 16 x 32 rows x (64 chunks + 1 slots) x (128 + 1) fp32
     assert f(16, 1, 32, 128, 16384, 256) == 16 * 32 * 65 * 128 * 4 + 16 * 32 * 65 * 4
-    assert f(1, 1, 1, 96, 10, 4) == 0          # unsupported head dim
+    assert f(1, 1, 1, 100, 10, 4) == 0         # unsupported head dim
     assert f(1, 1, 1, 64, 10, 0) == 0          # bad chunk
+    # head dims below a tile width are sized at the tile width
+    assert f(16, 1, 32, 80, 16384, 256) == f(16, 1, 32, 128, 16384, 256)
+    assert f(2, 3, 4, 320, 1000, 100) == f(2, 3, 4, 512, 1000, 100)
 
 
 def test_workspace_bytes_alignment(lib):
@@ -120,7 +124,7 @@ def test_workspace_bytes_alignment(lib):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(D=48), UNSUPPORTED), (dict(B=-1), INVALID), (dict(max_chunks=-1), INVALID),
+    (dict(D=48), UNSUPPORTED), (dict(D=96), UNSUPPORTED), (dict(B=-1), INVALID), (dict(max_chunks=-1), INVALID),
     (dict(o=None), INVALID), (dict(o_part=None), INVALID), (dict(B=0), OK),
 ])
 def test_combine_validation(lib, kw, want):
@@ -132,7 +136,7 @@ def test_combine_validation(lib, kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(D=40), UNSUPPORTED), (dict(page_size=3), UNSUPPORTED), (dict(table=None), INVALID),
+    (dict(D=44), UNSUPPORTED), (dict(page_size=3), UNSUPPORTED), (dict(table=None), INVALID),
     (dict(num_pages=0), INVALID), (dict(out=P + 2), INVALID), (dict(B=0), OK),
 ])
 def test_gather_validation(lib, kw, want):
@@ -150,7 +154,7 @@ def _st(a, b, c):
 def test_strided_prefill_validation(lib):
     f = lib.fa_prefill_strided
     def call(qs=None, ks=None, B=0):
-        return f(P, qs, P, ks, P, None, P, None, None, B, 8, 2, 16, 16, 128, 1, 0, 0.1, None, None)
+        return f(P, qs, P, ks, P, None, P, None, None, B, 8, 2, 16, 16, 128, 128, 1, 0, 0.1, None, None)
     assert call() == OK                                   # NULL strides: contiguous
     assert call(qs=_st(16 * 8 * 128, 8 * 128, 128)) == OK  # explicit dense strides
     assert call(qs=_st(16 * 8 * 128, 8 * 128, 12)) == INVALID    # head stride not a multiple of 8
@@ -162,7 +166,7 @@ def test_strided_prefill_validation(lib):
 def test_strided_decode_validation(lib):
     f = lib.fa_decode_paged_strided
     def call(ks=None, os_=None, B=0):
-        return f(P, None, P, ks, P, None, P, P, P, os_, None, B, 1, 8, 2, 128, 64, 16, 8, 64, 1, 0,
+        return f(P, None, P, ks, P, None, P, P, P, os_, None, B, 1, 8, 2, 128, 128, 64, 16, 8, 64, 1, 0,
                  0.1, None, P, 1 << 30, None)
     assert call() == OK
     assert call(ks=_st(2 * 16 * 2 * 128, 2 * 2 * 128, 128)) == OK      # K/V interleaved per slot
@@ -171,24 +175,24 @@ def test_strided_decode_validation(lib):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(D=80), UNSUPPORTED), (dict(page_size=3), UNSUPPORTED), (dict(Hkv=0), INVALID),
-    (dict(num_pages=0), INVALID), (dict(lens=None), INVALID), (dict(kc=P + 4), INVALID),
+    (dict(Dk=84), UNSUPPORTED), (dict(Dv=600), UNSUPPORTED), (dict(Dk=80, Dv=72, B=0), OK),
+    (dict(page_size=3), UNSUPPORTED), (dict(Hkv=0), INVALID), (dict(num_pages=0), INVALID), (dict(lens=None), INVALID), (dict(kc=P + 4), INVALID),
     (dict(kn=None), INVALID), (dict(ks=_st(0, 12, 8)), INVALID),
     (dict(B=0), OK), (dict(Snew=0), OK), (dict(table=None, num_pages=0, B=0), OK),
 ])
 def test_kv_append_validation(lib, kw, want):
     a = dict(kc=P, ks=None, vc=P, vs=None, table=P, lens=P, kn=P, kns=None, vn=P, vns=None,
-             B=2, Snew=4, Hkv=2, D=128, num_pages=64, page_size=16, max_pages=8)
+             B=2, Snew=4, Hkv=2, Dk=128, Dv=128, num_pages=64, page_size=16, max_pages=8)
     a.update(kw)
     assert lib.fa_kv_append(a["kc"], a["ks"], a["vc"], a["vs"], a["table"], a["lens"], a["kn"], a["kns"],
-                            a["vn"], a["vns"], a["B"], a["Snew"], a["Hkv"], a["D"], a["num_pages"],
+                            a["vn"], a["vns"], a["B"], a["Snew"], a["Hkv"], a["Dk"], a["Dv"], a["num_pages"],
                             a["page_size"], a["max_pages"], None) == want
 
 
 def test_score_mods_validation(lib):
     f = lib.fa_prefill_strided
     def call(m):
-        return f(P, None, P, None, P, None, P, None, None, 0, 8, 2, 16, 16, 128, 1, 0, 0.1,
+        return f(P, None, P, None, P, None, P, None, None, 0, 8, 2, 16, 16, 128, 128, 1, 0, 0.1,
                  ctypes.byref(m), None)
     assert call(_lib.ScoreMods(30.0, 8.0, P)) == OK
     assert call(_lib.ScoreMods(-1.0, 0.0, None)) == INVALID
@@ -200,3 +204,17 @@ def test_score_mods_validation(lib):
     assert call(_lib.ScoreMods(0.0, 0.0, None, P, 6, 4096)) == INVALID       # stride not a multiple of 4
     assert call(_lib.ScoreMods(0.0, 0.0, None, P, 0, -4)) == INVALID
     assert call(_lib.ScoreMods(0.0, 0.0, None, P, 1 << 40, 4)) == INVALID
+
+
+@pytest.mark.parametrize("dk,dv,want", [
+    (192, 128, OK), (320, 256, OK), (72, 80, OK), (8, 512, OK), (576, 512, UNSUPPORTED),
+    (128, 12, UNSUPPORTED), (0, 64, UNSUPPORTED),
+])
+def test_dk_dv_validation(lib, dk, dv, want):
+    """Distinct key / value head dims on the strided entry points (B = 0:
+    validation only)."""
+    f = lib.fa_prefill_strided
+    assert f(P, None, P, None, P, None, P, None, None, 0, 8, 2, 16, 16, dk, dv, 1, 0, 0.1, None, None) == want
+    g = lib.fa_decode_paged_strided
+    assert g(P, None, P, None, P, None, P, P, P, None, None, 0, 1, 8, 2, dk, dv, 64, 16, 8, 64, 1, 0,
+             0.1, None, P, 1 << 30, None) == want
