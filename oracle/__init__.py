@@ -15,3 +15,10 @@ from .attention import (  # noqa: F401
     to_f64,
     visible_mask,
 )
+from .fp8 import (  # noqa: F401
+    dequantize_e4m3,
+    e4m3_table,
+    e4m3_value,
+    kv_append_fp8_ref,
+    quantize_e4m3,
+)

@@ -8,9 +8,11 @@ import types
 import pytest
 
 from tests.oracle_pins import ALL_CHECKS
+from tests.test_oracle_fp8 import FP8_CHECKS
 from tests.test_oracle_mods import MOD_CHECKS
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+SRC_FP8 = os.path.join(os.path.dirname(SRC), "fp8.py")
 
 MUTATIONS = {
     "gqa head map h % Hkv": ("g = h // group", "g = h % Hkv"),
@@ -48,8 +50,8 @@ MUTATIONS = {
 }
 
 
-def _load_mutant(old, new):
-    with open(SRC) as f:
+def _load_mutant(old, new, path=SRC):
+    with open(path) as f:
         src = f.read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     mod = types.ModuleType("oracle_mutant")
@@ -68,6 +70,30 @@ def test_mutation_is_caught(name):
     mod = _load_mutant(*MUTATIONS[name])
     caught = []
     for check in ALL_CHECKS + MOD_CHECKS:
+        try:
+            check(mod)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(check.__name__)
+    assert caught, f"mutation '{name}' passed every pin"
+
+
+FP8_MUTATIONS = {
+    "exponent bias 8": ("2.0 ** (e - 7)", "2.0 ** (e - 8)"),
+    "subnormal scale": ("2.0 ** (1 - 7)", "2.0 ** (0 - 7)"),
+    "implicit one on subnormals": ("return sign * (m / 8.0) * 2.0 ** (1 - 7)", "return sign * (1.0 + m / 8.0) * 2.0 ** (1 - 7)"),
+    "ties away from zero": ("np.where(lo % 2 == 0, lo, hi)", "hi"),
+    "ties toward zero": ("np.where(lo % 2 == 0, lo, hi)", "lo"),
+    "sign dropped": ("codes | 0x80", "codes"),
+    "append token off by one": ("            t = n - snew + i\n", "            t = n - snew + i + 1\n"),
+    "append ignores the head scale": ("kq = quantize_e4m3(kn / ks[None, None, :, None])", "kq = quantize_e4m3(kn / ks[0])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
+def test_fp8_mutation_is_caught(name):
+    mod = _load_mutant(*FP8_MUTATIONS[name], path=SRC_FP8)
+    caught = []
+    for check in FP8_CHECKS:
         try:
             check(mod)
         except (AssertionError, ValueError, IndexError, FloatingPointError):
