@@ -16,6 +16,9 @@ each timed per call with the L2 / Infinity Cache flushed before the call,
 as algorithmic bytes (K and V of every visible token read once per KV head,
 plus Q, O, LSE, lengths and block table) over the call's duration.
 
+`--fp8` prints one JSON line with the decode and verify legs over fp8
+(OCP e4m3) K/V caches beside the same calls over bf16 caches.
+
 `--head-dims` prints one JSON line with prefill TFLOP/s and decode GB/s at
 head dims other than 64/128/256/512 and with Dk != Dv (same shapes as the
 prefill and decode workloads otherwise).
@@ -238,6 +241,60 @@ def cpu_baseline(workloads, inputs_cpu):
 
 
 # padded head dims and Dk != Dv, with the full tile widths (128, 256, 512) as references
+def bench_fp8(torch, fa, workloads, dev, steps, warmup):
+    """Decode (C3 shape) and verify (C5 shape) over fp8 caches: random finite
+    e4m3 codes and per-head scales (the timing does not depend on the
+    values), each call after the cache flush. Algorithmic bytes: one byte per
+    K and V element of every visible token once per KV head, plus Q, O, LSE,
+    lengths and block table; the bf16 call of the same shape is timed beside
+    it."""
+    out = {"mode": "fp8 KV cache", "n_gpus": 1, "steps": steps, "warmup": warmup}
+    flush = Flusher(torch, dev)
+    for shape in (workloads.C3, workloads.C5):
+        print(f"{shape.name} bf16", file=sys.stderr, flush=True)
+        ref = bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush)
+        torch.cuda.empty_cache()
+        print(f"{shape.name} fp8", file=sys.stderr, flush=True)
+        di = workloads.decode_inputs(shape)
+        g = torch.Generator("cpu").manual_seed(808)
+        kc = torch.randint(0, 0x7F, di.kcache.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+        kc |= (torch.rand(di.kcache.shape, generator=g) < 0.5).to(torch.uint8) << 7
+        vc = torch.randint(0, 0x7F, di.vcache.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+        vc |= (torch.rand(di.vcache.shape, generator=g) < 0.5).to(torch.uint8) << 7
+        kc, vc = kc.to(dev), vc.to(dev)
+        ks = torch.full((shape.Hkv,), 4.0 / 448, dtype=torch.float32, device=dev)
+        vs = torch.full((shape.Hkv,), 4.0 / 448, dtype=torch.float32, device=dev)
+        q = di.q.to(dev)
+        table = None if di.block_table is None else di.block_table.to(dev)
+        lens = di.seq_lens.to(dev)
+        ps = shape.page_size or 16
+        max_pages = di.block_table.shape[1] if table is not None else shape.max_len // ps
+        ws = torch.empty(fa.decode_workspace_bytes(shape.B, shape.Sq, shape.Hq, shape.D, max_pages * ps,
+                                                   shape.kv_chunk), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((shape.B, shape.Hq, shape.Sq), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.decode_paged_fp8(q, kc, vc, ks, vs, table, lens, page_size=ps, kv_chunk=shape.kv_chunk,
+                                causal=True, scale=shape.scale, workspace=ws, out=o, lse=lse)
+
+        for _ in range(warmup):
+            step()
+        per, _, _ = time_calls(torch, step, steps, flush=flush)
+        ms = sorted(per)[len(per) // 2]
+        bf16_bytes = decode_bytes(shape, di.seq_lens.tolist())
+        kv_bf16 = sum(int(n) for n in di.seq_lens.tolist()) * shape.Hkv * shape.D * 2 * 2
+        nbytes = bf16_bytes - kv_bf16 // 2
+        out[shape.name] = {"fp8_ms_per_call_median": round(ms, 4), "fp8_algorithmic_bytes": nbytes,
+                           "fp8_GB_s": round(nbytes / ms / 1e6, 1),
+                           "fp8_frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                           "bf16_ms_per_call_median": ref["ms_per_call_median"], "bf16_GB_s": ref["GB_s"],
+                           "speedup_vs_bf16": round(ref["ms_per_call_median"] / ms, 3)}
+        del kc, vc, q, ws, o, lse, table, lens
+        torch.cuda.empty_cache()
+    return out
+
+
 HEAD_DIMS = [(80, 80), (96, 96), (128, 128), (192, 128), (192, 192), (256, 256), (320, 256), (512, 512)]
 
 
@@ -354,6 +411,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and verify legs")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time decode and verify over fp8 KV caches instead of the headline")
     ap.add_argument("--head-dims", action="store_true",
                     help="time prefill and decode at other head dims and Dk != Dv instead of the headline")
     ap.add_argument("--mods", action="store_true",
@@ -387,6 +446,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    if args.fp8:
+        print(json.dumps(bench_fp8(torch, fa, workloads, dev, args.steps, args.warmup)), flush=True)
         return
 
     if args.head_dims:

@@ -14,8 +14,8 @@ import torch
 
 from ._lib import FAError, ScoreMods, check, load  # noqa: F401
 
-__all__ = ["prefill", "decode_paged", "decode_workspace_bytes", "combine_lse",
-           "kv_append", "paged_gather", "FAError", "load"]
+__all__ = ["prefill", "decode_paged", "decode_paged_fp8", "decode_workspace_bytes", "combine_lse",
+           "kv_append", "kv_append_fp8", "paged_gather", "FAError", "load"]
 
 
 def _ptr(t):
@@ -165,6 +165,87 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
                                          int(bool(causal)), int(window), float(scale), mref,
                                          _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, lse
+
+
+def _cache_geometry(kcache, vcache, block_table, page_size, dev):
+    if vcache.shape != kcache.shape:
+        raise ValueError("kcache and vcache differ in shape")
+    if block_table is not None:
+        _require(block_table, "block_table", torch.int32, dev)
+        if kcache.shape[1] != page_size:
+            raise ValueError("cache page dimension differs from page_size")
+        return kcache.shape[0], block_table.shape[1]
+    if kcache.shape[1] % page_size:
+        raise ValueError("contiguous cache length must be a multiple of page_size")
+    return 0, kcache.shape[1] // page_size
+
+
+def decode_paged_fp8(q, kcache, vcache, k_scale, v_scale, block_table, seq_lens, *, page_size: int = 16,
+                     kv_chunk: int = 256, causal: bool = True, window: int = 0,
+                     scale: float | None = None, workspace=None, out=None, lse=None,
+                     return_lse: bool = True, softcap: float = 0.0, max_bias: float = 0.0,
+                     sinks=None, mask=None):
+    """Split-KV decode / verify over fp8 (OCP e4m3) caches.
+
+    kcache / vcache: uint8 [num_pages, page_size, Hkv, 128] with block_table,
+    else [B, Smax, Hkv, 128] (views with a unit-stride last dimension);
+    k_scale / v_scale: fp32 [Hkv] dequantisation scales (value = e4m3(byte) *
+    scale). q and the result are bf16 [B, Sq, Hq, 128]; the rest is as
+    decode_paged.
+    """
+    B, Sq, Hq, D = q.shape
+    dev = q.device
+    _require(q, "q", torch.bfloat16, dev, strided=True)
+    _require(kcache, "kcache", torch.uint8, dev, strided=True)
+    _require(vcache, "vcache", torch.uint8, dev, strided=True)
+    _require(k_scale, "k_scale", torch.float32, dev)
+    _require(v_scale, "v_scale", torch.float32, dev)
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    Hkv = kcache.shape[2]
+    if kcache.shape[3] != D or k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("cache head dim or scale shape does not match")
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_bytes(B, Sq, Hq, D, max_pages * page_size, kv_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev, strided=True)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, max_pages * page_size, dev)
+    check(load().fa_decode_paged_fp8(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
+                                     _ptr(vcache), _strides(vcache), _ptr(k_scale), _ptr(v_scale),
+                                     _ptr(block_table), _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
+                                     B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
+                                     int(bool(causal)), int(window), float(scale), mref,
+                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, lse
+
+
+def kv_append_fp8(kcache, vcache, k_scale, v_scale, block_table, seq_lens, knew, vnew, *,
+                  page_size: int = 16):
+    """Quantise knew/vnew (bf16 [B, Snew, Hkv, D]) to e4m3 by the heads'
+    scales and write them into the uint8 caches in place (placement as
+    kv_append)."""
+    B, Snew, Hkv, D = knew.shape
+    dev = knew.device
+    for t, n in ((knew, "knew"), (vnew, "vnew")):
+        _require(t, n, torch.bfloat16, dev, strided=True)
+    for t, n in ((kcache, "kcache"), (vcache, "vcache")):
+        _require(t, n, torch.uint8, dev, strided=True)
+    _require(k_scale, "k_scale", torch.float32, dev)
+    _require(v_scale, "v_scale", torch.float32, dev)
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    if vnew.shape != knew.shape or kcache.shape[2:] != (Hkv, D):
+        raise ValueError("shape mismatch between caches and new rows")
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev)
+    check(load().fa_kv_append_fp8(_ptr(kcache), _strides(kcache), _ptr(vcache), _strides(vcache),
+                                  _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+                                  _ptr(knew), _strides(knew), _ptr(vnew), _strides(vnew),
+                                  B, Snew, Hkv, D, num_pages, page_size, max_pages, _stream(dev)))
 
 
 def combine_lse(o_part, lse_part, n_chunks=None, *, out=None, lse=None):

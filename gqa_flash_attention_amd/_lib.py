@@ -34,6 +34,10 @@ SIGNATURES = {
     "fa_decode_paged_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "fa_combine_lse": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_decode_paged_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+    "fa_kv_append_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_paged_gather": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),

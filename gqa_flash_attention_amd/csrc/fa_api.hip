@@ -80,13 +80,13 @@ bool get_mods(const fa_score_mods* m, Mods& out) {
   return true;
 }
 
-bool get_strides(const int64_t* st, Strides dense, bool kv, Strides& out) {
+bool get_strides(const int64_t* st, Strides dense, bool kv, Strides& out, int align = 8) {
   if (st == nullptr) {
     out = dense;
     return true;
   }
   for (int i = 0; i < 3; ++i)
-    if (st[i] < 0 || st[i] % 8 != 0 || st[i] >= (int64_t(1) << 40)) return false;
+    if (st[i] < 0 || st[i] % align != 0 || st[i] >= (int64_t(1) << 40)) return false;
   out = Strides{st[0], st[1], st[2]};
   return !(kv && out.token >= (int64_t(1) << 24));
 }
@@ -153,16 +153,24 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
   return o_bytes + l_bytes;
 }
 
-int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
-                            const void* kcache, const int64_t* k_stride,
-                            const void* vcache, const int64_t* v_stride,
-                            const int32_t* block_table, const int32_t* seq_lens,
-                            void* o, const int64_t* o_stride, float* lse,
-                            int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
-                            int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
-                            int causal, int window, float scale, const fa_score_mods* mods,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode / verify behind fa_decode_paged_strided (bf16 caches) and
+// fa_decode_paged_fp8 (one-byte e4m3 caches with per-head scales, D = 128).
+int decode_impl(const void* q, const int64_t* q_stride,
+                const void* kcache, const int64_t* k_stride,
+                const void* vcache, const int64_t* v_stride,
+                const float* k_scale, const float* v_scale, bool kv8,
+                const int32_t* block_table, const int32_t* seq_lens,
+                void* o, const int64_t* o_stride, float* lse,
+                int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
+                int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                int causal, int window, float scale, const fa_score_mods* mods,
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (kv8 && (Dk != 128 || Dv != 128)) return FA_ERR_UNSUPPORTED;
   Mods md;
   if (!get_mods(mods, md)) return FA_ERR_INVALID_ARG;
   if (max_pages_per_seq < 0 || kv_chunk <= 0) return FA_ERR_INVALID_ARG;
@@ -183,12 +191,18 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
     return block_table != nullptr ? Strides{(int64_t)page_size * Hkv * d, (int64_t)Hkv * d, d}
                                   : Strides{max_len * Hkv * d, (int64_t)Hkv * d, d};
   };
+  // fp8 cache rows are 16-byte aligned at 16 one-byte elements
+  const int calign = kv8 ? 16 : 8;
   if (!get_strides(q_stride, qd, false, qs) || !get_strides(o_stride, od, false, os) ||
-      !get_strides(k_stride, cache_dense(Dk), true, ks) || !get_strides(v_stride, cache_dense(Dv), true, vs))
+      !get_strides(k_stride, cache_dense(Dk), true, ks, calign) ||
+      !get_strides(v_stride, cache_dense(Dv), true, vs, calign))
     return FA_ERR_INVALID_ARG;
   if (B == 0 || Sq == 0) return FA_OK;
   if (!q || !o || !seq_lens || !aligned16(q) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (max_len > 0 && (!kcache || !vcache || !aligned16(kcache) || !aligned16(vcache)))
+    return FA_ERR_INVALID_ARG;
+  if (kv8 && (!k_scale || !v_scale || (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0 ||
+              (reinterpret_cast<uintptr_t>(v_scale) & 3u) != 0))
     return FA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   const size_t need = fa_decode_workspace_bytes(B, Sq, Hq, D, (int)max_len, kv_chunk);   // D = the tile width
@@ -212,13 +226,48 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
     SplitDesc sd{q, kcache, vcache, block_table, seq_lens, o_part, lse_part, qs, ks, vs,
                  B, Sq, Hq, Hkv, D, num_pages, page_shift, max_pages_per_seq, kv_chunk,
                  (int)n_slots, causal, window, Dk, Dv, scale, md.softcap, md.max_bias, md.mask, md.mask_sb,
-                 md.mask_ss};
+                 md.mask_ss, kv8, k_scale, v_scale};
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
   CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, md.sinks,
                  B, Sq, Hq, D, Dv};
   return to_status(launch_combine(cd, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
+                            const void* kcache, const int64_t* k_stride,
+                            const void* vcache, const int64_t* v_stride,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            void* o, const int64_t* o_stride, float* lse,
+                            int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
+                            int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                            int causal, int window, float scale, const fa_score_mods* mods,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_stride, kcache, k_stride, vcache, v_stride, nullptr, nullptr, false, block_table,
+                     seq_lens, o, o_stride, lse, B, Sq, Hq, Hkv, Dk, Dv, num_pages, page_size,
+                     max_pages_per_seq, kv_chunk, causal, window, scale, mods, workspace, workspace_bytes,
+                     stream);
+}
+
+int fa_decode_paged_fp8(const void* q, const int64_t* q_stride,
+                        const void* kcache, const int64_t* k_stride,
+                        const void* vcache, const int64_t* v_stride,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        void* o, const int64_t* o_stride, float* lse,
+                        int B, int Sq, int Hq, int Hkv, int D,
+                        int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                        int causal, int window, float scale, const fa_score_mods* mods,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_stride, kcache, k_stride, vcache, v_stride, k_scale, v_scale, true, block_table,
+                     seq_lens, o, o_stride, lse, B, Sq, Hq, Hkv, D, D, num_pages, page_size,
+                     max_pages_per_seq, kv_chunk, causal, window, scale, mods, workspace, workspace_bytes,
+                     stream);
 }
 
 int fa_decode_paged(const void* q, const void* kcache, const void* vcache,
@@ -277,6 +326,36 @@ int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int6
   AppendDesc d{kcache, vcache, knew, vnew, block_table, seq_lens, kcs, vcs, kns, vns,
                B, Snew, Hkv, Dk, Dv, num_pages, page_shift, max_pages_per_seq};
   return to_status(launch_append(d, static_cast<hipStream_t>(stream)));
+}
+
+int fa_kv_append_fp8(void* kcache, const int64_t* k_stride, void* vcache, const int64_t* v_stride,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
+                     int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
+                     void* stream) {
+  if (B < 0 || Snew < 0 || Hkv <= 0 || max_pages_per_seq < 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_ok(D) || D % 16 != 0) return FA_ERR_UNSUPPORTED;
+  const int page_shift = log2_exact(page_size);
+  if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
+  const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
+  if (max_len > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (block_table != nullptr && num_pages <= 0) return FA_ERR_INVALID_ARG;
+  Strides kcs, vcs, kns, vns;
+  const Strides cd = block_table != nullptr ? Strides{(int64_t)page_size * Hkv * D, (int64_t)Hkv * D, D}
+                                            : Strides{max_len * Hkv * D, (int64_t)Hkv * D, D};
+  const Strides nd{(int64_t)Snew * Hkv * D, (int64_t)Hkv * D, D};
+  if (!get_strides(k_stride, cd, false, kcs, 16) || !get_strides(v_stride, cd, false, vcs, 16) ||
+      !get_strides(knew_stride, nd, false, kns) || !get_strides(vnew_stride, nd, false, vns))
+    return FA_ERR_INVALID_ARG;
+  if (B == 0 || Snew == 0 || max_len == 0) return FA_OK;
+  if (!kcache || !vcache || !knew || !vnew || !seq_lens || !k_scale || !v_scale) return FA_ERR_INVALID_ARG;
+  if (!aligned16(kcache) || !aligned16(vcache) || !aligned16(knew) || !aligned16(vnew) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(v_scale) & 3u) != 0)
+    return FA_ERR_INVALID_ARG;
+  AppendFp8Desc d{kcache, vcache, knew, vnew, k_scale, v_scale, block_table, seq_lens, kcs, vcs, kns, vns,
+                  B, Snew, Hkv, D, num_pages, page_shift, max_pages_per_seq};
+  return to_status(launch_append_fp8(d, static_cast<hipStream_t>(stream)));
 }
 
 int fa_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,

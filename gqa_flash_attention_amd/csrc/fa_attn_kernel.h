@@ -109,6 +109,11 @@ struct AttnArgs {
   // (all of this in the padded kernels, MODS levels 3 and 4, which are used
   // exactly when dk < D or dv < D)
   int dk, dv;
+  // fp8 (OCP e4m3) K and V caches (kernels instantiated with KV8): the value
+  // of an element of KV head g is e4m3(byte) * k_scale[g] (v_scale[g] for V);
+  // device [Hkv]
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // Fill the score-modifier fields of the kernel arguments (host side).
@@ -211,7 +216,7 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
   return x;
 }
 
-template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, int MODS>
+template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, int MODS, bool KV8 = false>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
@@ -223,7 +228,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   constexpr bool kXform = MODS == 1 || MODS == 2 || MODS == 4;
   constexpr bool kMask = MODS == 2 || MODS == 4;
   constexpr bool kPad = MODS >= 3;
-  constexpr int KCH = D / 8;                  // 16-byte chunks per row
+  // fp8 K/V (one byte per element) only in the one-wave-per-32-rows split
+  // kernels at D = 128 (8 chunks of 16 bytes per key row)
+  static_assert(!KV8 || (SPLIT && DS == 1 && D == 128 && !kPad), "fp8 K/V: D = 128 split kernels");
+  constexpr int ES = KV8 ? 1 : 2;             // bytes per K/V element
+  constexpr int KCH = D * ES / 16;            // 16-byte chunks per row
   constexpr int NSEG = BN * KCH / 64;         // 1 KiB segments per tile
   static_assert(NSEG % NW == 0, "every wave loads whole segments");
   constexpr int SEGW = NSEG / NW;             // segments per wave per operand
@@ -241,13 +250,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // A ring of NBUF tile buffers per operand, each its own object: the copies
   // into one never alias reads of another, so no read waits on a copy it does
   // not need.
-  constexpr int B2 = NBUF > 2 ? BN * D : 8, B3 = NBUF > 3 ? BN * D : 8;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BN * D];
+  constexpr int TU = BN * D * ES / 2;          // 16-bit slots of one tile buffer
+  constexpr int B2 = NBUF > 2 ? TU : 8, B3 = NBUF > 3 ? TU : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[TU];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[TU];
   __shared__ __attribute__((aligned(1024))) uint16_t sK2[B2];
   __shared__ __attribute__((aligned(1024))) uint16_t sK3[B3];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[TU];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[TU];
   __shared__ __attribute__((aligned(1024))) uint16_t sV2[B2];
   __shared__ __attribute__((aligned(1024))) uint16_t sV3[B3];
   int* sT = nullptr;
@@ -279,13 +289,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   constexpr bool KEEP_SEG = SEGW <= 8;
   constexpr int NKEEP = KEEP_SEG ? SEGW : 1;
   auto seg_row = [&](int i) -> int { return ((wave * SEGW + i) * 64 + lane) / KCH; };
+  // fp8 tiles: rows of 8 chunks, the chunk XORed with the row's low 3 bits
+  auto swzk = [](int row) -> int { return KV8 ? (row & 7) : swz_k<D>(row); };
+  auto swzv = [](int row) -> int { return KV8 ? (row & 7) : swz_v<D>(row); };
   auto seg_koff = [&](int i) -> uint32_t {
     const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
-    return 2u * (uint32_t)(row * k_rs + 8 * (pc ^ swz_k<D>(row)));
+    return (uint32_t)(ES * row * k_rs + 16 * (pc ^ swzk(row)));
   };
   auto seg_voff = [&](int i) -> uint32_t {
     const int pos = (wave * SEGW + i) * 64 + lane, row = pos / KCH, pc = pos % KCH;
-    return 2u * (uint32_t)(row * v_rs + 8 * (pc ^ swz_v<D>(row)));
+    return (uint32_t)(ES * row * v_rs + 16 * (pc ^ swzv(row)));
   };
   int srow[NKEEP];         // key row (inside the tile) of each of this lane's segments
   uint32_t koff[NKEEP];    // byte offset of its K chunk inside an unclamped tile
@@ -356,12 +369,12 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         }
         const int64_t base = (int64_t)page * (is_v ? a.v_sb : a.k_sb) +
                              (int64_t)((t & ((1 << a.page_shift) - 1)) - row) * rs;
-        src = reinterpret_cast<const char*>(kv_base + base) + off0;
+        src = reinterpret_cast<const char*>(kv_base) + ES * base + off0;
       } else {
         // uniform tile base + 32-bit per-lane byte offset
         uint32_t o = off0;
-        if (tail && row > lim) o -= 2u * (uint32_t)((row - lim) * rs);
-        src = reinterpret_cast<const char*>(kv_base + (int64_t)tb * rs) + o;
+        if (tail && row > lim) o -= (uint32_t)(ES * (row - lim) * rs);
+        src = reinterpret_cast<const char*>(kv_base) + ES * ((int64_t)tb * rs) + o;
       }
       if constexpr (kPad) src -= seg_pad(i, is_v);
       dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
@@ -374,8 +387,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       koff += (int64_t)b_t * a.k_sb;
       voff += (int64_t)b_t * a.v_sb;
     }
-    kb_out = a.k + koff;
-    vb_out = a.v + voff;
+    kb_out = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.k) + ES * koff);
+    vb_out = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.v) + ES * voff);
   };
 
   // ---- the rows being worked on: one block of rows of one (b, KV head) ------
@@ -442,8 +455,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   float l_run = 0.f;         // this lane's part of the row sum
   // exponent factor: scores are raw q.k (scale folded in here), or with
   // score modifiers already scaled and modified (natural units)
-  const float sl2 = kXform ? kLog2e : a.sl2;
-  const float thr = kRescaleLog2 / sl2;
+  // (fp8 K: times the KV head's K scale, set once the head is known)
+  float sl2 = kXform ? kLog2e : a.sl2;
+  float thr = kRescaleLog2 / sl2;
+  float xscale = a.scale;    // the score scale of the score transform
+  float vsc = 1.f;           // fp8 V: the KV head's V scale
 
   // S^T (this wave's part of the contraction) for the tile in bk
   auto scores = [&](const uint16_t* bk, f32x16 (&s)[NKB]) {
@@ -500,7 +516,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          float v = s[kb][x] * a.scale;
+          float v = s[kb][x] * xscale;
           if (a.softcap > 0.f) {
             // tanh y = 1 - 2 / (1 + e^(2y)), finite for every y
             const float e2 = fast_exp2(2.0f * kLog2e * v * inv_cap);
@@ -637,6 +653,55 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         }
       }
   };
+  // fp8 tiles (KV8): K rows are read 8 bytes (8 d values) per lane and
+  // widened to bf16; V^T comes from ds_read_b64_tr_b8: the lane in position
+  // (group G, r = 2 k + a) of each 16-lane group addresses key 16 ks +
+  // 8 (k / 4) + 4 (G / 2) + k % 4 at d 32 db + 16 (G % 2) + 8 a, so that lane
+  // l receives V[key][32 db + l % 32] for its 8 keys in the order of the P^T
+  // operand (keys 4 hl + 0..3, then 8 + 4 hl + 0..3 of the 16-key step).
+  // The fragments stay as fp8 bytes in registers (half the registers of
+  // bf16) and are widened just before their MFMA.
+  auto read_k8 = [&](const uint16_t* bk, u32x2 (&kr)[NQC][NKB]) {
+    const unsigned char* b8 = reinterpret_cast<const unsigned char*>(bk);
+#pragma unroll
+    for (int c = 0; c < NQC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = 32 * kb + j;
+        kr[c][kb] = *reinterpret_cast<const u32x2*>(b8 + row * D + 16 * (c ^ swzk(row)) + 8 * hl);
+      }
+  };
+  auto scores_regs8 = [&](const u32x2 (&kr)[NQC][NKB], f32x16 (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 s0{}, s1{};
+#pragma unroll
+      for (int c = 0; c < NQC; c += 2) {
+        s0 = mfma32(as_bf16x8(fp8x8_to_bf16x8(kr[c][kb])), qf[c], s0);
+        if (c + 1 < NQC) s1 = mfma32(as_bf16x8(fp8x8_to_bf16x8(kr[c + 1][kb])), qf[c + 1], s1);
+      }
+      s[kb] = s0 + s1;
+    }
+  };
+  auto read_v8 = [&](const uint16_t* bv, u32x2 (&vr)[NKS][NDB]) {
+    const unsigned char* b8 = reinterpret_cast<const unsigned char*>(bv);
+    const int grp = lane >> 4, r16 = lane & 15, aa = r16 & 1, kk = r16 >> 1;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row = 16 * ks + 8 * (kk >> 2) + 4 * (grp >> 1) + (kk & 3);
+        const int lc = 2 * db + (grp & 1);
+        vr[ks][db] = read_tr8(b8 + row * D + 16 * (lc ^ swzv(row)) + 8 * aa);
+      }
+  };
+  auto accumulate_regs8 = [&](const u32x2 (&vr)[NKS][NDB], const u32x4 (&pf)[NKS]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(as_bf16x8(fp8x8_to_bf16x8(vr[ks][db])), as_bf16x8(pf[ks]), oacc[db]);
+  };
   auto accumulate_regs = [&](const u32x4 (&vr)[NKS][NDB], const u32x4 (&pf)[NKS]) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -711,7 +776,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     auto write_partial = [&](int s_) {
       const float l_tot = pair_sum(l_run);
       const bool empty = !(l_tot > 0.f);
-      const float inv = empty ? 0.f : fast_rcp(l_tot);
+      const float inv = empty ? 0.f : fast_rcp(l_tot) * vsc;
       const float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
       if (row_ok) {
         const int64_t prow = slot_index(s_);
@@ -792,6 +857,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // (the grid is a multiple of Hkv workgroups)
     const int g_w = w % a.Hkv;
     const int sets = W / a.Hkv;
+    if constexpr (KV8) {
+      // fold the head's K scale into the exponent factor (or the score scale)
+      const float ksc = a.k_scale[g_w];
+      vsc = a.v_scale[g_w];
+      if constexpr (kXform) xscale = a.scale * ksc;
+      else sl2 = a.sl2 * ksc;
+      thr = kRescaleLog2 / sl2;
+    }
     // a range holds at least one chunk, so the rows of a sequence meet at
     // most (its chunks + 1) ranges
     const int per = (int)max(((int64_t)T + sets - 1) / sets, (int64_t)tpc);
@@ -964,8 +1037,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         wait_e(it + NBUF - 1 < n_loc);
         __syncthreads();
         load_mask(tb);
-        u32x4 kr[NQC][NKB];
-        read_k(kbuf(u), kr);
+        // K(t) fragments in registers (raw fp8 bytes for an fp8 cache)
+        u32x4 kr[KV8 ? 1 : NQC][KV8 ? 1 : NKB];
+        u32x2 kr8[KV8 ? NQC : 1][KV8 ? NKB : 1];
+        if constexpr (KV8) read_k8(kbuf(u), kr8);
+        else read_k(kbuf(u), kr);
         wait_lgkm0();
         if constexpr (NW > 1) __syncthreads();     // every wave has read K(t)
         __builtin_amdgcn_sched_barrier(0);
@@ -975,20 +1051,24 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         }
         ke = tile_ke(cu);
         f32x16 sc[NKB];
-        scores_regs(kr, sc);
+        if constexpr (KV8) scores_regs8(kr8, sc);
+        else scores_regs(kr, sc);
         const float nb = prepare(sc, tb);
         u32x4 pv[NKS];
         exponentiate(sc, nb, pv);
         // V(t) landed (copies issued after it: the tiles behind and K(t + NBUF))
         wait_e(it + NBUF < n_loc);
         __syncthreads();
-        u32x4 vr[NKS][NDB];
-        read_v(vbuf(u), vr);
+        u32x4 vr[KV8 ? 1 : NKS][KV8 ? 1 : NDB];
+        u32x2 vr8[KV8 ? NKS : 1][KV8 ? NDB : 1];
+        if constexpr (KV8) read_v8(vbuf(u), vr8);
+        else read_v(vbuf(u), vr);
         wait_lgkm0();
         if constexpr (NW > 1) __syncthreads();     // every wave has read V(t)
         __builtin_amdgcn_sched_barrier(0);
         if (it + NBUF < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf(u));
-        accumulate_regs(vr, pv);
+        if constexpr (KV8) accumulate_regs8(vr8, pv);
+        else accumulate_regs(vr, pv);
       } else {
         // The copy order after the prologue is, per step t, V(t + NBUF - 1)
         // (refilling tile t-1's V buffer) then K(t + NBUF).

@@ -33,6 +33,16 @@ template <int D, int NWR> struct SplitCfg {
   // tile buffers per operand: two keep 3/4 of the ring in flight; larger
   // head dims are LDS-bound
   static constexpr int NBUF = 2;
+  // fp8 tiles are half the bytes. One-wave workgroups keep two buffers: 18
+  // KiB of LDS lets a CU hold eight of them, two waves per SIMD, with as many
+  // bytes in flight as four bf16 workgroups (the one-wave kernel is bound by
+  // the latency of its own step, so a second wave per SIMD is what pays).
+  // Wider workgroups are held by registers at two waves per SIMD and take
+  // deeper rings instead (three for the paged two-wave kernel, which holds
+  // no more within its register budget).
+  static constexpr int NBUF8 = NW == 1 ? 2 : 4;
+  static constexpr int NBUF8P = NW == 1 ? 2 : (NW == 2 ? 3 : 4);
+  static constexpr int WPE8 = 2;
 };
 
 // Workgroups of a kernel the GPU holds at once: CUs x resident workgroups per
@@ -40,7 +50,7 @@ template <int D, int NWR> struct SplitCfg {
 // workgroups of 32 KiB or less (the occupancy query allows 160), so the
 // count is the smaller of the two.
 template <typename Kernel>
-int resident_workgroups(Kernel kernel, int threads, int (&cache)[16]) {
+int resident_workgroups(Kernel kernel, int threads, int* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (cache[dev] > 0) return cache[dev];
@@ -79,6 +89,8 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   a.sl2 = d.scale * kLog2e;
   a.dk = d.dk;
   a.dv = d.dv;
+  a.k_scale = d.k_scale;
+  a.v_scale = d.v_scale;
   set_mods(a, d.scale, d.softcap, d.max_bias, nullptr, d.Hq, d.mask, d.mask_sb, d.mask_ss);
   const int64_t rows = (int64_t)d.Sq * a.G;
   a.n_rb = (int)((rows + BM - 1) / BM);
@@ -103,10 +115,27 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
        attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 3>,
        attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 4>}};
   const int paged = d.table != nullptr ? 1 : 0;
-  const K k = kernels[paged][level];
+  K k = kernels[paged][level];
+  int* cache_row;
   // the grid is what the chosen kernel holds resident
   static int cache[2][5][16];
-  const int resident = resident_workgroups(k, NW * 64, cache[paged][level]);
+  cache_row = cache[paged][level];
+  if constexpr (D == 128) {
+    if (d.kv8) {
+      // fp8 caches: plain, or score transform and mask (softcap / ALiBi alone
+      // run with a null mask)
+      static const K kernels8[2][2] = {
+          {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE8, 0, true>,
+           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE_MASK, 2, true>},
+          {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE8, 0, true>,
+           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE_MASK, 2, true>}};
+      static int cache8[2][2][16];
+      const int l8 = level == 0 ? 0 : 1;
+      k = kernels8[paged][l8];
+      cache_row = cache8[paged][l8];
+    }
+  }
+  const int resident = resident_workgroups(k, NW * 64, cache_row);
   // whole sets of Hkv workgroups, one per KV head
   const int grid = std::max(resident / d.Hkv, 1) * d.Hkv;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);

@@ -134,6 +134,32 @@ __device__ __forceinline__ u32x2 read_tr16(const uint16_t* lds) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Transposing LDS read of eight 8-bit values (ds_read_b64_tr_b8). Within
+// each group of 16 lanes, lane i receives byte i % 8 of the 8-byte rows
+// addressed by lanes i / 8, i / 8 + 2, ..., i / 8 + 14 (in that order) of the
+// group (measured on gfx950).
+__device__ __forceinline__ u32x2 read_tr8(const unsigned char* lds) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)lds);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Eight OCP e4m3 (fp8) values, byte k of w = element k, as eight bf16 in the
+// same order. gfx950's v_cvt_pk_f32_fp8 decodes OCP e4m3 exactly (checked on
+// all 256 codes), and every e4m3 value is exact in bf16.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
+    r[2 * h] = pack_bf16(lo[0], lo[1]);
+    r[2 * h + 1] = pack_bf16(hi[0], hi[1]);
+  }
+  return r;
+}
+
 // Element offset of K/V row (sequence b, token t, KV head g) in a cache laid
 // out as pages [num_pages, page_size, Hkv, D] reached through block_table
 // [B, max_pages], or, with no table, as a contiguous [B, slots, Hkv, D]

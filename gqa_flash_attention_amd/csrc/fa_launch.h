@@ -35,6 +35,9 @@ struct SplitDesc {
   float softcap, max_bias;            // 0 = off (sinks are the combine's)
   const void* mask;                   // device bf16 additive mask (token positions) or null
   int64_t mask_sb, mask_ss;
+  bool kv8;                           // fp8 (OCP e4m3) caches, D = 128
+  const float* k_scale;               // kv8: device [Hkv] dequantisation scales
+  const float* v_scale;
 };
 
 struct CombineDesc {
@@ -56,6 +59,14 @@ struct AppendDesc {
   int B, Snew, Hkv, dk, dv, num_pages, page_shift, max_pages;   // dk, dv: multiples of 8
 };
 
+struct AppendFp8Desc {
+  void* kcache; void* vcache; const void* knew; const void* vnew;   // caches: one byte per element
+  const float* k_scale; const float* v_scale;                         // device [Hkv]
+  const int32_t* table; const int32_t* seq_lens;
+  Strides kcs, vcs, kns, vns;
+  int B, Snew, Hkv, D, num_pages, page_shift, max_pages;
+};
+
 struct GatherDesc {
   const void* cache; const int32_t* table; const int32_t* seq_lens; void* out;
   int B, Hkv, D, num_pages, page_shift, max_pages;
@@ -67,5 +78,6 @@ hipError_t launch_split(const SplitDesc& d, hipStream_t stream);
 hipError_t launch_combine(const CombineDesc& d, hipStream_t stream);
 hipError_t launch_gather(const GatherDesc& d, hipStream_t stream);
 hipError_t launch_append(const AppendDesc& d, hipStream_t stream);
+hipError_t launch_append_fp8(const AppendFp8Desc& d, hipStream_t stream);
 
 }  // namespace gqafa

@@ -214,6 +214,40 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode / verify over an fp8 KV cache: fa_decode_paged_strided with K and V
+ * stored one byte per element in the OCP e4m3 format (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; no infinities; largest finite 448) and
+ * one fp32 dequantisation scale per KV head: the cached value of an element
+ * of KV head g is e4m3(byte) * k_scale[g] (v_scale[g] for V). Halving the
+ * bytes of the cache halves the HBM traffic of the memory-bound split
+ * kernel. (The pages name low-bit KV caches, q8_0 in the llama.cpp PR 28507
+ * report and KVarN in beellama.cpp PR 149, without fixing a format; e4m3
+ * with a per-head scale is the format gfx950 converts natively.)
+ *
+ *   kcache, vcache  uint8 [num_pages, page_size, Hkv, D] with block_table,
+ *                   else [B, max_pages_per_seq * page_size, Hkv, D]
+ *   k_stride, v_stride  host int64[3] strides in elements (= bytes), NULL
+ *                   for the contiguous layout; multiples of 16 below 2^40,
+ *                   token strides below 2^24
+ *   k_scale, v_scale    device fp32 [Hkv], 4-byte aligned
+ *   D               128 (FA_ERR_UNSUPPORTED otherwise)
+ * Everything else (q and o bf16, seq_lens, block table, workspace, score
+ * modifiers, outputs) is as fa_decode_paged_strided with Dk = Dv = D. The
+ * arithmetic is that of the bf16 cache path on the dequantised values: the
+ * K scale multiplies the exponent factor, the V scale the normalisation.
+ */
+int fa_decode_paged_fp8(const void* q, const int64_t* q_stride,
+                        const void* kcache, const int64_t* k_stride,
+                        const void* vcache, const int64_t* v_stride,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        void* o, const int64_t* o_stride, float* lse,
+                        int B, int Sq, int Hq, int Hkv, int D,
+                        int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                        int causal, int window, float scale, const fa_score_mods* mods,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Merge split-KV partials by their LSE:
  *   M = max_c LSE_c,  LSE = M + ln sum_c exp(LSE_c - M),
  *   O = sum_c exp(LSE_c - LSE) * O_c.
@@ -261,6 +295,27 @@ int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int6
                  const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
                  int B, int Snew, int Hkv, int Dk, int Dv, int num_pages, int page_size,
                  int max_pages_per_seq, void* stream);
+
+/*
+ * fa_kv_append into an fp8 cache (see fa_decode_paged_fp8): each new bf16
+ * value v of KV head g is stored as the e4m3 code nearest to the fp32
+ * quotient v / scale[g] (one IEEE fp32 division, rounded to nearest even),
+ * ties to the even code, saturating at +-448 (NaN -> 0x7f; the sign of the
+ * quotient is kept, so -0 and negatives that round to 0 give 0x80).
+ *
+ *   kcache, vcache  uint8 caches as in fa_decode_paged_fp8, written in place;
+ *                   strides multiples of 16 (bytes)
+ *   k_scale, v_scale    device fp32 [Hkv] (the dequantisation scales)
+ *   knew, vnew      bf16 [B, Snew, Hkv, D], strides as fa_kv_append
+ *   D               a multiple of 16 in [16, 512]
+ * Placement, skipped rows and races are as in fa_kv_append.
+ */
+int fa_kv_append_fp8(void* kcache, const int64_t* k_stride, void* vcache, const int64_t* v_stride,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
+                     int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
+                     void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["fa_prefill", "fa_prefill_strided", "fa_decode_workspace_bytes",
                             "fa_decode_paged", "fa_decode_paged_strided", "fa_combine_lse",
-                            "fa_kv_append", "fa_status_string", "fa_paged_gather"])
+                            "fa_kv_append", "fa_status_string", "fa_paged_gather",
+                            "fa_decode_paged_fp8", "fa_kv_append_fp8"])
     assert set(names) == set(_lib.SIGNATURES)
 
 
@@ -218,3 +219,25 @@ def test_dk_dv_validation(lib, dk, dv, want):
     g = lib.fa_decode_paged_strided
     assert g(P, None, P, None, P, None, P, P, P, None, None, 0, 1, 8, 2, dk, dv, 64, 16, 8, 64, 1, 0,
              0.1, None, P, 1 << 30, None) == want
+
+
+def test_fp8_decode_validation(lib):
+    f = lib.fa_decode_paged_fp8
+    def call(D=128, ks=None, ksc=P, vsc=P, B=0):
+        return f(P, None, P, ks, P, None, ksc, vsc, P, P, P, None, None, B, 1, 8, 2, D, 64, 16, 8, 64, 1, 0,
+                 0.1, None, P, 1 << 30, None)
+    assert call() == OK
+    assert call(D=64) == UNSUPPORTED and call(D=256) == UNSUPPORTED
+    assert call(ks=_st(0, 2 * 2 * 128, 128)) == OK           # K/V interleaved per slot, 16-byte rows
+    assert call(ks=_st(0, 8 * 2, 8)) == INVALID              # not a multiple of 16 bytes
+    assert call(B=2, ksc=None) == INVALID and call(B=2, vsc=P + 2) == INVALID
+
+
+def test_fp8_append_validation(lib):
+    f = lib.fa_kv_append_fp8
+    def call(D=128, ksc=P, B=2, kc=P, ks=None):
+        return f(kc, ks, P, None, ksc, P, P, P, P, None, P, None, B, 4, 2, D, 64, 16, 8, None)
+    assert call(D=72) == UNSUPPORTED and call(D=600) == UNSUPPORTED
+    assert call(ksc=None) == INVALID and call(ksc=P + 1) == INVALID
+    assert call(kc=P + 8) == INVALID and call(ks=_st(0, 8, 8)) == INVALID
+    assert call(B=0) == OK and call(D=80, B=0) == OK

@@ -1,0 +1,194 @@
+"""fp8 (OCP e4m3) KV caches through the C ABI: the quantising append must
+produce the oracle's codes byte for byte (values from subnormal to
+saturating, per-head scales, paged and contiguous caches), and decode /
+verify over fp8 caches must match the fp64 oracle on the dequantised cache
+at the usual tolerances (NaN codes past each sequence's end, score
+modifiers, the full-size decode workload on sampled rows)."""
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_flash_attention_amd as fa
+import oracle
+import workloads
+from tests.gpu_util import DEV, assert_parity, to_np
+
+pytestmark = pytest.mark.gpu
+
+NAN_CODE = 0x7F
+
+
+def _quantized_cache(gen, shape, scale):
+    """uint8 codes of N(0,1) bf16 values quantised by the oracle with the
+    per-head scales (shape [..., Hkv, D])."""
+    x = torch.randn(shape, generator=gen).to(torch.bfloat16).float().numpy()
+    q = x.astype(np.float32) / scale.numpy().astype(np.float32)[:, None]
+    return torch.from_numpy(oracle.quantize_e4m3(q))
+
+
+def _scales(gen, Hkv, base):
+    return (base * torch.exp(0.5 * torch.randn(Hkv, generator=gen))).float()
+
+
+def _deq(codes, scale):
+    return oracle.dequantize_e4m3(codes.numpy(), scale.numpy())
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_fp8_append_bitexact(paged):
+    print(f"fp8 append paged={paged}", flush=True)
+    g = torch.Generator().manual_seed(71 + int(paged))
+    B, Snew, Hkv, D, ps, mp = 4, 8, 4, 128, 16, 10
+    P = B * mp + 3
+    if paged:
+        table = torch.randperm(P, generator=g)[: B * mp].reshape(B, mp).to(torch.int32)
+        table[3, 0] = -1                                   # out of range: sequence 3's first page skipped
+        kc = torch.randint(0, 256, (P, ps, Hkv, D), generator=g, dtype=torch.int32).to(torch.uint8)
+    else:
+        table = None
+        kc = torch.randint(0, 256, (B, mp * ps, Hkv, D), generator=g, dtype=torch.int32).to(torch.uint8)
+    vc = torch.randint(0, 256, kc.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    lens = torch.tensor([mp * ps, 37, 5, 12], dtype=torch.int32)
+    # magnitudes from 1e-6 (subnormal codes and zero) to 1e4 (saturating)
+    mag = torch.pow(10.0, torch.empty(B, Snew, Hkv, D).uniform_(-6, 4, generator=g))
+    kn = (torch.randn(B, Snew, Hkv, D, generator=g) * mag).to(torch.bfloat16)
+    vn = (torch.randn(B, Snew, Hkv, D, generator=g) * mag).to(torch.bfloat16)
+    kn[0, 0, 0, :4] = torch.tensor([0.0, -0.0, float("inf"), float("-inf")], dtype=torch.bfloat16)
+    ks = torch.tensor([0.5, 0.01, 3.0, 1.0], dtype=torch.float32)
+    vs = torch.tensor([0.25, 2.0, 0.003, 1.0], dtype=torch.float32)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    fa.kv_append_fp8(kd, vd, ks.to(DEV), vs.to(DEV), None if table is None else table.to(DEV), lens.to(DEV),
+                     kn.to(DEV), vn.to(DEV), page_size=ps)
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.kv_append_fp8_ref(kc.numpy(), vc.numpy(), None if table is None else table.numpy(),
+                                            lens.numpy(), kn, vn, ks.numpy(), vs.numpy(), page_size=ps)
+    kg, vg = kd.cpu().numpy(), vd.cpu().numpy()
+    bad = np.argwhere(kg != k_ref)
+    assert bad.size == 0, f"{len(bad)} K codes differ, first at {bad[:3].tolist()}"
+    assert np.array_equal(vg, v_ref)
+
+
+DECODE = [
+    # B, Sq, Hq, Hkv, page_size (0 = contiguous), max_len, len range, chunk
+    (4, 1, 32, 8, 0, 2048, (1, 2048), 256),
+    (3, 1, 16, 4, 16, 1024, (1, 1024), 128),
+    (2, 8, 64, 8, 16, 1024, (8, 1024), 256),           # verify: 64 rows per KV head
+    (2, 4, 32, 4, 32, 768, (4, 768), 96),
+    (2, 2, 8, 1, 64, 256, (0, 256), 64),                # zero-length sequences possible
+    (40, 2, 8, 4, 16, 4096, (1, 4096), 32),             # several ranges per workgroup set
+]
+
+
+def _fp8_case(case, seed):
+    B, Sq, Hq, Hkv, ps, max_len, (lo, hi), chunk = case
+    shape = workloads.DecodeShape("fp8", B=B, Sq=Sq, Hq=Hq, Hkv=Hkv, D=128, page_size=ps, max_len=max_len,
+                                  len_lo=lo, len_hi=hi, kv_chunk=chunk, seed=seed)
+    di = workloads.decode_inputs(shape)
+    g = torch.Generator().manual_seed(seed + 1)
+    ks, vs = _scales(g, Hkv, 4.0 / 448), _scales(g, Hkv, 4.0 / 448)
+    kc = _quantized_cache(g, di.kcache.shape, ks)
+    vc = _quantized_cache(g, di.vcache.shape, vs)
+    # NaN codes in every slot past each sequence's end
+    lens = di.seq_lens.tolist()
+    for b, n in enumerate(lens):
+        if di.block_table is None:
+            kc[b, n:] = NAN_CODE
+            vc[b, n:] = NAN_CODE
+        else:
+            for t in range(n, di.block_table.shape[1] * ps):
+                page = int(di.block_table[b, t // ps])
+                kc[page, t % ps] = NAN_CODE
+                vc[page, t % ps] = NAN_CODE
+    return shape, di, kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "B{}_Sq{}_H{}x{}_ps{}_L{}_{}_c{}".format(*c))
+def test_fp8_decode(case):
+    print(f"fp8 decode {case}", flush=True)
+    shape, di, kc, vc, ks, vs = _fp8_case(case, seed=case[0] * 13 + case[1])
+    ps = shape.page_size or 16
+    table = None if di.block_table is None else di.block_table.to(DEV)
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV), table,
+                                 di.seq_lens.to(DEV), page_size=ps, kv_chunk=shape.kv_chunk, causal=True,
+                                 scale=shape.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, _deq(kc, ks), _deq(vc, vs), di.block_table, di.seq_lens,
+                                             page_size=ps, causal=True, scale=shape.scale)
+    assert_parity(o, lse, o_ref, lse_ref, f"fp8 decode {case}")
+
+
+def test_fp8_verify_all_modifiers():
+    case = (2, 8, 32, 4, 16, 768, (300, 768), 256)
+    shape, di, kc, vc, ks, vs = _fp8_case(case, seed=501)
+    g = torch.Generator().manual_seed(502)
+    sinks = torch.randn(shape.Hq, generator=g).float()
+    mask = (2.0 * torch.randn(shape.B, shape.Sq, shape.max_len, generator=g)).to(torch.bfloat16)
+    mask[:, :, 3:9] = -float("inf")
+    kw = dict(softcap=20.0, max_bias=4.0)
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV),
+                                 di.block_table.to(DEV), di.seq_lens.to(DEV), page_size=16, kv_chunk=256,
+                                 causal=True, scale=shape.scale, sinks=sinks.to(DEV), mask=mask.to(DEV), **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, _deq(kc, ks), _deq(vc, vs), di.block_table, di.seq_lens,
+                                             page_size=16, causal=True, scale=shape.scale,
+                                             sinks=sinks.double().numpy(), mask=mask, **kw)
+    assert_parity(o, lse, o_ref, lse_ref, "fp8 verify all modifiers")
+
+
+def test_fp8_append_then_decode():
+    g = torch.Generator().manual_seed(601)
+    B, Sq, Hq, Hkv, D, ps, mp = 2, 4, 16, 2, 128, 16, 20
+    P = B * mp
+    table = torch.randperm(P, generator=g).reshape(B, mp).to(torch.int32)
+    ks, vs = _scales(g, Hkv, 3.0 / 448), _scales(g, Hkv, 3.0 / 448)
+    kc = _quantized_cache(g, (P, ps, Hkv, D), ks)
+    vc = _quantized_cache(g, (P, ps, Hkv, D), vs)
+    lens = torch.tensor([mp * ps - 7, 150], dtype=torch.int32)
+    kn = torch.randn(B, Sq, Hkv, D, generator=g).to(torch.bfloat16)
+    vn = torch.randn(B, Sq, Hkv, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, Sq, Hq, D, generator=g).to(torch.bfloat16)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    fa.kv_append_fp8(kd, vd, ks.to(DEV), vs.to(DEV), table.to(DEV), lens.to(DEV), kn.to(DEV), vn.to(DEV),
+                     page_size=ps)
+    o, lse = fa.decode_paged_fp8(q.to(DEV), kd, vd, ks.to(DEV), vs.to(DEV), table.to(DEV), lens.to(DEV),
+                                 page_size=ps, kv_chunk=128)
+    torch.cuda.synchronize()
+    k2, v2 = oracle.kv_append_fp8_ref(kc.numpy(), vc.numpy(), table.numpy(), lens.numpy(), kn, vn,
+                                      ks.numpy(), vs.numpy(), page_size=ps)
+    assert np.array_equal(kd.cpu().numpy(), k2) and np.array_equal(vd.cpu().numpy(), v2)
+    o_ref, lse_ref = oracle.decode_paged_ref(q, oracle.dequantize_e4m3(k2, ks.numpy()),
+                                             oracle.dequantize_e4m3(v2, vs.numpy()), table, lens, page_size=ps,
+                                             causal=True, scale=1.0 / np.sqrt(D))
+    assert_parity(o, lse, o_ref, lse_ref, "fp8 append + decode")
+
+
+def test_fp8_decode_c3_shape_sampled():
+    """The 1-row decode workload at full size over an fp8 cache: sampled
+    sequences and heads against the oracle."""
+    s = workloads.C3
+    di = workloads.decode_inputs(s)
+    g = torch.Generator().manual_seed(701)
+    ks, vs = _scales(g, s.Hkv, 4.0 / 448), _scales(g, s.Hkv, 4.0 / 448)
+    # each sequence's valid tokens quantised by the oracle; NaN codes past its end
+    kq = torch.full(di.kcache.shape, NAN_CODE, dtype=torch.uint8)
+    vq = torch.full(di.vcache.shape, NAN_CODE, dtype=torch.uint8)
+    ksn, vsn = ks.numpy().astype(np.float32)[:, None], vs.numpy().astype(np.float32)[:, None]
+    for b in range(s.B):
+        n = int(di.seq_lens[b])
+        kq[b, :n] = torch.from_numpy(oracle.quantize_e4m3(di.kcache[b, :n].float().numpy() / ksn))
+        vq[b, :n] = torch.from_numpy(oracle.quantize_e4m3(di.vcache[b, :n].float().numpy() / vsn))
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kq.to(DEV), vq.to(DEV), ks.to(DEV), vs.to(DEV), None,
+                                 di.seq_lens.to(DEV), page_size=16, kv_chunk=s.kv_chunk, causal=True,
+                                 scale=s.scale)
+    torch.cuda.synchronize()
+    o, lse = to_np(o), to_np(lse)
+    heads = sorted({0, 5, s.Hq // 2, s.Hq - 1})
+    for b in sorted({0, s.B // 2, s.B - 1}):
+        n = int(di.seq_lens[b])
+        kd = oracle.dequantize_e4m3(kq[b:b + 1, :n].numpy(), ks.numpy())
+        vd = oracle.dequantize_e4m3(vq[b:b + 1, :n].numpy(), vs.numpy())
+        o_ref, lse_ref = oracle.decode_paged_ref(di.q[b:b + 1], kd, vd, None, di.seq_lens[b:b + 1],
+                                                 page_size=16, causal=True, scale=s.scale, heads=heads)
+        assert_parity(o[b:b + 1][:, :, heads], lse[b:b + 1][:, heads], o_ref[:, :, heads], lse_ref[:, heads],
+                      f"fp8 C3 b{b}")
