@@ -20,7 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgqafa.so")
-SOURCES = ["fa_prefill.hip", "fa_decode.hip", "fa_cache.hip", "fa_api.hip"]
+SOURCES = ["fa_split_d128.hip", "fa_split_d64.hip", "fa_split_d256.hip", "fa_split_d512.hip",
+           "fa_prefill.hip", "fa_decode.hip", "fa_cache.hip", "fa_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

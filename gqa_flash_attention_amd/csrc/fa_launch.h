@@ -78,6 +78,11 @@ hipError_t launch_split(const SplitDesc& d, hipStream_t stream);
 hipError_t launch_combine(const CombineDesc& d, hipStream_t stream);
 hipError_t launch_gather(const GatherDesc& d, hipStream_t stream);
 hipError_t launch_append(const AppendDesc& d, hipStream_t stream);
+// split kernels of one tile width each (fa_split_d*.hip)
+hipError_t launch_split_d64(const SplitDesc& d, hipStream_t stream);
+hipError_t launch_split_d128(const SplitDesc& d, hipStream_t stream);
+hipError_t launch_split_d256(const SplitDesc& d, hipStream_t stream);
+hipError_t launch_split_d512(const SplitDesc& d, hipStream_t stream);
 hipError_t launch_append_fp8(const AppendFp8Desc& d, hipStream_t stream);
 
 }  // namespace gqafa

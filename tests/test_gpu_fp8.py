@@ -192,3 +192,30 @@ def test_fp8_decode_c3_shape_sampled():
                                                  page_size=16, causal=True, scale=s.scale, heads=heads)
         assert_parity(o[b:b + 1][:, :, heads], lse[b:b + 1][:, heads], o_ref[:, :, heads], lse_ref[:, heads],
                       f"fp8 C3 b{b}")
+
+
+def test_fp8_interleaved_cache_bitwise():
+    """K and V interleaved per slot in one uint8 allocation (strided views)
+    give the same bits as separate contiguous caches."""
+    case = (3, 4, 32, 4, 16, 512, (4, 512), 128)
+    shape, di, kc, vc, ks, vs = _fp8_case(case, seed=901)
+    both = torch.stack([kc, vc], dim=2).to(DEV)          # [pages, slot, 2, Hkv, D]
+    args = (ks.to(DEV), vs.to(DEV), di.block_table.to(DEV), di.seq_lens.to(DEV))
+    o1, l1 = fa.decode_paged_fp8(di.q.to(DEV), both[:, :, 0], both[:, :, 1], *args, page_size=16,
+                                 kv_chunk=128, scale=shape.scale)
+    o2, l2 = fa.decode_paged_fp8(di.q.to(DEV), kc.to(DEV), vc.to(DEV), *args, page_size=16, kv_chunk=128,
+                                 scale=shape.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_fp8_decode_window():
+    case = (2, 8, 64, 8, 16, 1024, (8, 1024), 256)
+    shape, di, kc, vc, ks, vs = _fp8_case(case, seed=911)
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV),
+                                 di.block_table.to(DEV), di.seq_lens.to(DEV), page_size=16, kv_chunk=256,
+                                 causal=True, window=100, scale=shape.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, _deq(kc, ks), _deq(vc, vs), di.block_table, di.seq_lens,
+                                             page_size=16, causal=True, window=100, scale=shape.scale)
+    assert_parity(o, lse, o_ref, lse_ref, "fp8 verify window 100")

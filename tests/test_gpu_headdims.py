@@ -158,3 +158,35 @@ def test_append_then_verify_dk_dv():
     o_ref, lse_ref = oracle.decode_paged_ref(q, kc2, vc2, table, lens, page_size=ps, causal=True,
                                              scale=1.0 / np.sqrt(Dk))
     assert_parity(o, lse, o_ref, lse_ref, "append + verify 192/128")
+
+
+def test_prefill_padded_with_mask_and_window():
+    """The padded kernel with the score transform and a mask (level 4):
+    80/64 with softcap, ALiBi, sinks, a mask and a window."""
+    B, Sq, Skv, Hq, Hkv, Dk, Dv = 2, 90, 120, 8, 2, 80, 64
+    g = torch.Generator().manual_seed(41)
+    q, k, v = _randn(g, (B, Sq, Hq, Dk)), _randn(g, (B, Skv, Hkv, Dk)), _randn(g, (B, Skv, Hkv, Dv))
+    sinks = torch.randn(Hq, generator=g).float()
+    mask = (2.0 * torch.randn(B, Sq, 124, generator=g)).to(torch.bfloat16)
+    mask[:, :, 30:40] = -float("inf")
+    scale = 1.0 / np.sqrt(Dk)
+    kw = dict(softcap=15.0, max_bias=6.0)
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, window=50, scale=scale,
+                        sinks=sinks.to(DEV), mask=mask.to(DEV)[:, :, :Skv], **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, causal=True, window=50, scale=scale,
+                                          sinks=sinks.double().numpy(), mask=mask[:, :, :Skv], **kw)
+    assert_parity(o, lse, o_ref, lse_ref, "prefill 80/64 all modifiers window 50")
+
+
+def test_decode_padded_window():
+    B, Sq, Hq, Hkv, Dk, Dv, ps, max_len = 2, 4, 16, 4, 96, 96, 16, 640
+    q, kc, vc, table, lens_t, kd, vd = _decode_case(B, Sq, Hq, Hkv, Dk, Dv, ps, max_len, [640, 333],
+                                                    seed=51, paged=True)
+    scale = 1.0 / np.sqrt(Dk)
+    o, lse = fa.decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV), lens_t.to(DEV), page_size=ps,
+                             kv_chunk=128, causal=True, window=70, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q, torch.nan_to_num(kd.float()), torch.nan_to_num(vd.float()),
+                                          causal=True, window=70, scale=scale, seq_lens=[640, 333])
+    assert_parity(o, lse, o_ref, lse_ref, "decode 96/96 window 70")
