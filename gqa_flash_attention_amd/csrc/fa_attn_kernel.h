@@ -30,10 +30,10 @@
 //
 // Staging. K and V tiles are copied by global_load_lds_dwordx4: each lane's
 // 16-byte load lands at (segment base + 16 * lane) in LDS, so a swizzled LDS
-// layout is produced by choosing WHICH global chunk each lane fetches. Two
-// LDS buffers per operand (separate objects) let the loads of tile t+1 run
-// while tile t is computed, with one barrier per tile; no registers hold the
-// tile in flight.
+// layout is produced by choosing WHICH global chunk each lane fetches. A ring
+// of NBUF LDS buffers per operand (separate objects; two for bf16 tiles) lets
+// the loads of the next tiles run while tile t is computed, with one barrier
+// per tile; no registers hold the tile in flight.
 //
 // D split (DS = 2, used for the large head dims): two waves share the same 32
 // rows; each holds half of Q's head dim and half of O. Each computes the
@@ -54,6 +54,17 @@
 // online softmax (an incremental LSE combine) and writes one partial per
 // block of rows it touches, in slot r - r0 of those rows (r the range, r0 the
 // range of the rows' first tile); the LSE combine merges the partials.
+//
+// Forms. MODS selects what the score path does: 0 plain (the softmax scale
+// rides in the exponent FMA; sinks, when given, are folded in by the prefill
+// epilogue or the combine); 1 the score transform (logit softcap, ALiBi
+// slope); 2 the transform plus an additive bf16 mask; 3 and 4 are 0 and 2 on
+// head dims below the tile width D (Q columns past Dk load as 0, K/V chunks
+// past Dk / Dv are filled from chunk 0 of the same key row, O columns past
+// Dv are not stored). KV8 (split kernels at D = 128) reads one-byte OCP e4m3
+// K/V tiles and widens each fragment to bf16 just before its MFMA; the K/V
+// scales of the workgroup's KV head fold into the exponent factor and the
+// partial's normalisation.
 #pragma once
 
 #include "fa_device.h"
