@@ -364,6 +364,31 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const int pf = tb >> a.page_shift, pl = (tb + min(lim, BN - 1)) >> a.page_shift;
       if (b_t != tw_b || pf < tw_p0 || pl >= tw_p0 + TAB) stage_table(b_t, pf);
     }
+    if constexpr (PAGED && TAB > 0 && BN == 32 && !kPad) {
+      // A whole tile starting on a 16-token boundary with pages of 16 tokens
+      // or more: rows 0-15 lie in one page and rows 16-31 in one page (the
+      // same one for larger pages), so both row bases are wave-uniform
+      // (scalar arithmetic) and a lane only picks one and adds its 32-bit
+      // offset inside the tile.
+      if (!tail && a.page_shift >= 4 && (tb & 15) == 0) {
+        const int mask = (1 << a.page_shift) - 1;
+        const int p0 = __builtin_amdgcn_readfirstlane(sT[(tb >> a.page_shift) - tw_p0]);
+        const int p1 = __builtin_amdgcn_readfirstlane(sT[((tb + 16) >> a.page_shift) - tw_p0]);
+        const int64_t sb = is_v ? a.v_sb : a.k_sb;
+        const char* base0 = reinterpret_cast<const char*>(kv_base) +
+                            ES * ((int64_t)p0 * sb + (int64_t)(tb & mask) * rs);
+        const char* base1 = reinterpret_cast<const char*>(kv_base) +
+                            ES * ((int64_t)p1 * sb + (int64_t)((tb + 16) & mask) * rs - 16 * (int64_t)rs);
+#pragma unroll
+        for (int i = 0; i < SEGW; ++i) {
+          const int row = KEEP_SEG ? srow[i] : seg_row(i);
+          const uint32_t off0 = KEEP_SEG ? (is_v ? voff[i] : koff[i]) : (is_v ? seg_voff(i) : seg_koff(i));
+          const char* src = (row >= 16 ? base1 : base0) + off0;
+          dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dst + (wave * SEGW + i) * 512);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < SEGW; ++i) {
       const int row = KEEP_SEG ? srow[i] : seg_row(i);
