@@ -155,3 +155,56 @@ def test_verify_c5_full_size_sampled():
     o_ref, lse_ref = _ref(di, s, heads=heads)
     assert_parity(to_np(o)[:, :, heads], to_np(lse)[:, heads], o_ref[:, :, heads], lse_ref[:, heads],
                   "C5 sampled heads")
+
+
+def _ws_for(shape, fill=None):
+    ps = shape.page_size or 16
+    n = fa.decode_workspace_bytes(shape.B, shape.Sq, shape.Hq, shape.D, shape.max_len, shape.kv_chunk)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    if fill is not None:
+        ws.view(torch.float32)[: n // 4].fill_(fill)
+    return ws
+
+
+@pytest.mark.parametrize("mods", [False, True])
+def test_decode_deterministic(mods):
+    """Repeated calls give the same bits (the split depends only on shapes,
+    lengths and the GPU)."""
+    shape = workloads.DecodeShape("det", B=6, Sq=4, Hq=32, Hkv=8, D=128, page_size=16, max_len=2048,
+                                  len_lo=1, len_hi=2048, kv_chunk=256, seed=31)
+    di = workloads.decode_inputs(shape)
+    kw = dict(softcap=25.0, max_bias=6.0, sinks=torch.randn(32).to(DEV)) if mods else {}
+    o1, l1 = _decode(di, shape, **kw)
+    o2, l2 = _decode(di, shape, **kw)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_decode_poisoned_workspace():
+    """A workspace full of NaN before the call changes nothing: the combine
+    reads only slots written by this call."""
+    shape = workloads.DecodeShape("poison", B=5, Sq=8, Hq=64, Hkv=8, D=128, page_size=16, max_len=1536,
+                                  len_lo=0, len_hi=1536, kv_chunk=128, seed=33)
+    di = workloads.decode_inputs(shape)
+    o1, l1 = _decode(di, shape, workspace=_ws_for(shape, fill=0.0))
+    o2, l2 = _decode(di, shape, workspace=_ws_for(shape, fill=float("nan")))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    o_ref, lse_ref = _ref(di, shape)
+    assert_parity(o2, l2, o_ref, lse_ref, "decode with a NaN-filled workspace")
+
+
+def test_decode_workspace_reused_across_shapes():
+    """One workspace serves a large call and then smaller ones: no stale
+    partial of the earlier call leaks into a later one."""
+    big = workloads.DecodeShape("big", B=8, Sq=8, Hq=32, Hkv=4, D=128, page_size=16, max_len=4096,
+                                len_lo=2000, len_hi=4096, kv_chunk=128, seed=35)
+    ws = _ws_for(big)
+    _decode(workloads.decode_inputs(big), big, workspace=ws)
+    for i, (B, Sq, Hq, Hkv, D, L, chunk) in enumerate([(3, 2, 16, 4, 128, 1024, 256), (2, 8, 32, 4, 64, 512, 64),
+                                                        (4, 1, 32, 8, 128, 3000 // 16 * 16, 128)]):
+        small = workloads.DecodeShape("small", B=B, Sq=Sq, Hq=Hq, Hkv=Hkv, D=D, page_size=16, max_len=L,
+                                      len_lo=0, len_hi=L, kv_chunk=chunk, seed=36 + i)
+        di = workloads.decode_inputs(small)
+        assert fa.decode_workspace_bytes(B, Sq, Hq, D, L, chunk) <= ws.numel()
+        o1, l1 = _decode(di, small, workspace=ws)
+        o2, l2 = _decode(di, small, workspace=_ws_for(small, fill=0.0))
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2), i
