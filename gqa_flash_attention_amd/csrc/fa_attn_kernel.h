@@ -338,13 +338,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // load. A tile outside the window restages it (all waves together).
   int tw_b = -1, tw_p0 = 0;
   auto stage_table = [&](int b_t, int pf) {
-    __syncthreads();                          // every wave is done with the old window
+    lds_barrier();                          // every wave is done with the old window
     const int np = min(TAB, a.max_pages - pf);
     for (int i = tid; i < np; i += NW * 64) {
       const int page = a.table[(int64_t)b_t * a.max_pages + pf + i];
       sT[i] = min(max(page, 0), a.num_pages - 1);
     }
-    __syncthreads();
+    lds_barrier();
     tw_b = b_t;
     tw_p0 = pf;
   };
@@ -482,6 +482,33 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // (V[key_base + e][d_base + i], e = 0..3).
   const int m16 = lane & 15;
   const int g1 = (lane >> 4) & 1;
+  // Element offset of this lane's V^T read inside a tile buffer, per 32-wide
+  // d block; the read of 16-key step ks and half h adds (16 ks + 8 h) D (the
+  // V swizzle depends on row & 3, the same for every ks and h). The offsets
+  // are opaque to the optimiser, so every read address stays one constant
+  // away from its buffer and the compiler can tell which buffer a read
+  // touches: otherwise it loses track on long address chains and makes the
+  // read wait for every tile copy in flight, whatever buffer they fill.
+  // The kernels for head dims below D, short of registers, compute each
+  // address in full instead.
+  int vlo[kPad ? 1 : NDB];
+  if constexpr (!kPad) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
+      const int r0 = 4 * hl + (m16 >> 2);
+      vlo[db] = r0 * D + 8 * ((d >> 3) ^ swz_v<D>(r0)) + (d & 7);
+    }
+  }
+  auto v_elem = [&](int ks, int half, int db) -> int {
+    if constexpr (kPad) {
+      const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
+      const int row = 16 * ks + 8 * half + 4 * hl + (m16 >> 2);
+      return row * D + 8 * ((d >> 3) ^ swz_v<D>(row)) + (d & 7);
+    } else {
+      return (16 * ks + 8 * half) * D + vlo[db];
+    }
+  };
 
   // ---- running state -----------------------------------------------------
   f32x16 oacc[NDB];
@@ -631,13 +658,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         // consecutive MFMAs feed different accumulators
-        const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
-        const int dch = d >> 3, dsub = d & 7;
         u32x4 vw;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int row = 16 * ks + 8 * half + 4 * hl + (m16 >> 2);
-          const u32x2 t = read_tr16(&bv[row * D + 8 * (dch ^ swz_v<D>(row)) + dsub]);
+          const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
           vw[2 * half] = t[0];
           vw[2 * half + 1] = t[1];
         }
@@ -678,12 +702,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * (db + dh * NDB) + 16 * g1 + 4 * (m16 & 3);
-        const int dch = d >> 3, dsub = d & 7;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int row = 16 * ks + 8 * half + 4 * hl + (m16 >> 2);
-          const u32x2 t = read_tr16(&bv[row * D + 8 * (dch ^ swz_v<D>(row)) + dsub]);
+          const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
           vr[ks][db][2 * half] = t[0];
           vr[ks][db][2 * half + 1] = t[1];
         }
@@ -1071,7 +1092,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       if constexpr (EARLY) {
         // K(t) landed (copies issued after it: V(t) and the tiles behind)
         wait_e(it + NBUF - 1 < n_loc);
-        __syncthreads();
+        lds_barrier();
         load_mask(tb);
         // K(t) fragments in registers (raw fp8 bytes for an fp8 cache)
         u32x4 kr[KV8 ? 1 : NQC][KV8 ? 1 : NKB];
@@ -1079,7 +1100,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         if constexpr (KV8) read_k8(kbuf(u), kr8);
         else read_k(kbuf(u), kr);
         wait_lgkm0();
-        if constexpr (NW > 1) __syncthreads();     // every wave has read K(t)
+        if constexpr (NW > 1) lds_barrier();     // every wave has read K(t)
         __builtin_amdgcn_sched_barrier(0);
         if (it + NBUF < n_loc) {
           issue_next_k(kbuf(u));
@@ -1094,13 +1115,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         exponentiate(sc, nb, pv);
         // V(t) landed (copies issued after it: the tiles behind and K(t + NBUF))
         wait_e(it + NBUF < n_loc);
-        __syncthreads();
+        lds_barrier();
         u32x4 vr[KV8 ? 1 : NKS][KV8 ? 1 : NDB];
         u32x2 vr8[KV8 ? NKS : 1][KV8 ? NDB : 1];
         if constexpr (KV8) read_v8(vbuf(u), vr8);
         else read_v(vbuf(u), vr);
         wait_lgkm0();
-        if constexpr (NW > 1) __syncthreads();     // every wave has read V(t)
+        if constexpr (NW > 1) lds_barrier();     // every wave has read V(t)
         __builtin_amdgcn_sched_barrier(0);
         if (it + NBUF < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf(u));
         if constexpr (KV8) accumulate_regs8(vr8, pv);
@@ -1112,7 +1133,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // K(t) landed in every wave's share; every wave is done with the PV
         // product of tile t-1, whose V buffer is refilled next
         if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
-        __syncthreads();
+        lds_barrier();
         load_mask(tb);
         if (it >= 1 && it + NBUF - 1 < n_loc) issue(d_tb, d_ke, d_vb, d_b, true, vbuf((u + NBUF - 1) % NBUF));
         ke = tile_ke(cu);
@@ -1120,7 +1141,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         scores(kbuf(u), sc);
         if constexpr (DS > 1) {
           publish(sc, it & 1);
-          __syncthreads();
+          lds_barrier();
           combine_partner(sc, it & 1);
         }
         const float nb = prepare(sc, tb);
@@ -1128,7 +1149,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         exponentiate(sc, nb, pv);
         // V(t) landed; every wave is done with K(t), whose buffer is refilled
         if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
-        __syncthreads();
+        lds_barrier();
         if (it + NBUF < n_loc) {
           issue_next_k(kbuf(u));
           if (it + NBUF + 1 < n_loc) it_next(pf);
@@ -1197,14 +1218,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
       }
       if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
-      __syncthreads();
+      lds_barrier();
       scores(kbuf(0), sc);
       publish(sc, 0);
     }
     auto step = [&](int it, int u) {
       const int tb = t_start + it * BN;
       if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
-      __syncthreads();
+      lds_barrier();
       load_mask(tb);
       if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
       if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));

@@ -116,6 +116,19 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
+// Workgroup barrier that orders LDS accesses only. The waves of these kernels
+// hand tiles to each other through LDS and never read each other's global
+// writes, so a barrier need not wait for the wave's outstanding global
+// loads, stores or LDS copies; the explicit waits in front of each barrier
+// cover the copies it hands over. __syncthreads() orders global memory too,
+// which makes every barrier after a global store wait for every copy in
+// flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wait until every LDS (and scalar-memory) access of this wave has completed:
 // s_waitcnt lgkmcnt(0), leaving vmcnt and expcnt at their maxima.
 __device__ __forceinline__ void wait_lgkm0() {
