@@ -116,25 +116,28 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
-// Workgroup barrier that orders LDS accesses only. The waves of these kernels
-// hand tiles to each other through LDS and never read each other's global
-// writes, so a barrier need not wait for the wave's outstanding global
-// loads, stores or LDS copies; the explicit waits in front of each barrier
-// cover the copies it hands over. __syncthreads() orders global memory too,
-// which makes every barrier after a global store wait for every copy in
-// flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Wait until every LDS (and scalar-memory) access of this wave has completed:
 // s_waitcnt lgkmcnt(0), leaving vmcnt and expcnt at their maxima.
 __device__ __forceinline__ void wait_lgkm0() {
   constexpr int imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);
   __builtin_amdgcn_s_waitcnt(imm);
 }
+
+// Workgroup barrier for handing LDS over between the waves of these kernels:
+// the wave's own LDS reads and writes are complete (lgkmcnt 0), the compiler
+// moves no memory access across it, and every wave arrives. It does not wait
+// for global loads, stores or global -> LDS copies: the waves never read
+// each other's global writes, and each barrier that hands over a copied tile
+// follows an explicit wait for that tile's copies. A fenced barrier
+// (__syncthreads, or a release fence on LDS) would wait for every copy in
+// flight, since copies into LDS count as LDS writes.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 
 // Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16). Within
 // each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows
