@@ -410,6 +410,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // uniform tile base + 32-bit per-lane byte offset
         uint32_t o = off0;
         if (tail && row > lim) o -= (uint32_t)(ES * (row - lim) * rs);
+        if constexpr (!SPLIT) {
+          // prefill: the buffer form, which keeps its operand reads in flight
+          // (measured slower for the split kernels' streams)
+          if constexpr (kPad) o -= seg_pad(i, is_v);
+          dma16_buf<SPLIT>(reinterpret_cast<const char*>(kv_base) + ES * ((int64_t)tb * rs), o,
+                           dst + (wave * SEGW + i) * 512);
+          continue;
+        }
         src = reinterpret_cast<const char*>(kv_base) + ES * ((int64_t)tb * rs) + o;
       }
       if constexpr (kPad) src -= seg_pad(i, is_v);

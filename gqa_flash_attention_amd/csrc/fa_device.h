@@ -81,6 +81,23 @@ __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_seg) {
                                    STREAM ? kNonTemporal : 0);
 }
 
+// The same copy through a buffer resource: 16 bytes from base + voffset
+// (this lane's byte offset) into this lane's 16 bytes of the LDS segment.
+// After a copy in the global (flat-encoded) form the compiler treats every
+// LDS read as possibly out of order and makes each use wait for all of
+// them (lgkmcnt 0); after the buffer form its LDS waits stay graded, so
+// operand reads issued ahead of their MFMAs stay in flight. Range checking
+// is off (the copies stay in range by construction); descriptor word 3 is
+// the gfx9-family default.
+template <bool STREAM>
+__device__ __forceinline__ void dma16_buf(const void* base, uint32_t voffset, uint16_t* lds_seg) {
+  constexpr int kNonTemporal = 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_seg, 16,
+                                           voffset, 0, 0, STREAM ? kNonTemporal : 0);
+}
+
 // Scheduling hints (sched_group_barrier masks: 0x2 VALU, 0x8 MFMA, 0x100
 // DS read). One pipeline step: N1 MFMAs that each consume R1 LDS reads and
 // may hide V1 VALU instructions, then N2 MFMAs consuming R2 reads each. The
