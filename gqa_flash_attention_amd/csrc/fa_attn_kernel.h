@@ -28,9 +28,11 @@
 // the V^T operand comes straight from the row-major V tile through the
 // transposing LDS read ds_read_b64_tr_b16.
 //
-// Staging. K and V tiles are copied by global_load_lds_dwordx4: each lane's
-// 16-byte load lands at (segment base + 16 * lane) in LDS, so a swizzled LDS
-// layout is produced by choosing WHICH global chunk each lane fetches. A ring
+// Staging. K and V tiles are copied straight into LDS, 16 bytes per lane
+// (global_load_lds_dwordx4 in the split kernels, buffer_load_dwordx4 ... lds
+// in prefill): each lane's load lands at (segment base + 16 * lane), so a
+// swizzled LDS layout is produced by choosing WHICH global chunk each lane
+// fetches. A ring
 // of NBUF LDS buffers per operand (separate objects; two for bf16 tiles) lets
 // the loads of the next tiles run while tile t is computed, with one barrier
 // per tile; no registers hold the tile in flight.
@@ -1032,8 +1034,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // it lands and the buffer is refilled once all have read it (the refill
     // then does not wait for the tile's MFMAs and softmax): per step
     // K(t + NBUF) right after K(t) is read, V(t + NBUF) right after V(t) is
-    // read, so at every wait 2 NBUF - 1 of the 2 NBUF buffers are being
-    // filled.
+    // read, so with the ring kept full 2 NBUF - 1 of the 2 NBUF buffers are
+    // being filled at every wait (how far the waits let copies run ahead is
+    // chosen per kernel below).
     constexpr bool EARLY = DS == 1;
     constexpr int AHEAD_E = (2 * NBUF - 1) * SEGW < 63 ? (2 * NBUF - 1) * SEGW : 63;
     // Stores count in vmcnt too, in issue order with the copies: after a
