@@ -23,6 +23,11 @@ plus Q, O, LSE, lengths and block table) over the call's duration.
 head dims other than 64/128/256/512 and with Dk != Dv (same shapes as the
 prefill and decode workloads otherwise).
 
+`--configs` prints one JSON line with every seeded workload timed the same
+way: the four prefill shapes (tiny causal, the headline, head dim 256 with a
+1024-token window, head dim 512 causal) in TFLOP/s and the decode and verify
+shapes in GB/s, each with its fraction of the MI355X peak.
+
 `--mods` instead prints one JSON line with the cost of each score modifier
 (logit softcap, ALiBi, sinks, an additive mask, all four) on the same three
 workloads, timed the same way.
@@ -202,6 +207,46 @@ def bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush, mods=No
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "kv_chunk": shape.kv_chunk, "cache": "flushed before each call (1 GiB write)",
             "sum_seq_len": int(di.seq_lens.sum())}
+
+
+def bench_prefill_shape(torch, fa, dev, s, inputs, steps, warmup):
+    """Median per-call time of one prefill shape (inputs already on the GPU)."""
+    q, k, v = inputs
+    o = torch.empty_like(q)
+    lse = torch.empty((s.B, s.Hq, s.Sq), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.prefill(q, k, v, causal=s.causal, window=s.window, scale=s.scale, out=o, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    per, _, _ = time_calls(torch, step, steps)
+    ms = sorted(per)[len(per) // 2]
+    flops = prefill_flops(s)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": s.name, "ms_per_call_median": round(ms, 4), "algorithmic_flop": flops,
+            "TFLOP_s": round(tflops, 1), "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_configs(torch, fa, workloads, dev, steps, warmup):
+    out = {"mode": "configs", "n_gpus": 1, "steps": steps, "warmup": warmup}
+    for s, make in ((workloads.C1, lambda: workloads.prefill_inputs(workloads.C1)),
+                    (workloads.C2, lambda: workloads.prefill_inputs(workloads.C2))):
+        inputs = [t.to(dev) for t in make()]
+        out[s.name] = bench_prefill_shape(torch, fa, dev, s, inputs, steps, warmup)
+        del inputs
+    a, b = workloads.c4_inputs()
+    for s, cpu in ((workloads.C4A, a), (workloads.C4B, b)):
+        inputs = [t.to(dev) for t in cpu]
+        out[s.name] = bench_prefill_shape(torch, fa, dev, s, inputs, steps, warmup)
+        del inputs
+        torch.cuda.empty_cache()
+    del a, b
+    flush = Flusher(torch, dev)
+    for s in (workloads.C3, workloads.C5):
+        out[s.name] = bench_decode(torch, fa, workloads, dev, s, steps, warmup, flush)
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(workloads, inputs_cpu):
@@ -408,13 +453,18 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    # untimed calls before each timed leg: the shader clock climbs for the
+    # first ~0.1-0.5 s of sustained load (measured on MI355X: the headline
+    # prefill at 930 TFLOP/s after 30 calls, 1010 after 0.5 s of calls)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and verify legs")
     ap.add_argument("--fp8", action="store_true",
                     help="time decode and verify over fp8 KV caches instead of the headline")
     ap.add_argument("--head-dims", action="store_true",
                     help="time prefill and decode at other head dims and Dk != Dv instead of the headline")
+    ap.add_argument("--configs", action="store_true",
+                    help="time all six seeded workloads (four prefill, decode, verify) instead of the headline")
     ap.add_argument("--mods", action="store_true",
                     help="time the score modifiers on the three workloads instead of the headline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -454,6 +504,10 @@ def main():
 
     if args.head_dims:
         print(json.dumps(bench_head_dims(torch, fa, workloads, dev, args.steps, args.warmup)), flush=True)
+        return
+
+    if args.configs:
+        print(json.dumps(bench_configs(torch, fa, workloads, dev, args.steps, args.warmup)), flush=True)
         return
 
     if args.mods:
