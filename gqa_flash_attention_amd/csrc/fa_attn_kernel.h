@@ -1230,6 +1230,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // lets the groups issued after group t stay outstanding. Buffer indices
     // are compile-time constants in the unrolled ring.
     constexpr int GROUP = 2 * SEGW;                         // copy instructions per group
+    constexpr bool kPrioMfma = D <= 128;
     constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
     constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
     f32x16 sc[NKB];
@@ -1255,6 +1256,12 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       combine_partner(sc, it & 1);
       const float nb = prepare(sc, tb);
       f32x16 sn[NKB];
+      // Up to D = 128 two workgroups share a CU, so each SIMD runs waves of
+      // both. A wave raises its priority for its MFMA block and drops it for
+      // the softmax bookkeeping and barrier that follow, so the issue
+      // arbiter feeds the matrix cores first (measured +2.4 % at head dim
+      // 128; with one workgroup per CU it gains nothing).
+      if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(1);
       scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
       u32x4 pf[NKS];
       exponentiate(sc, nb, pf);
@@ -1264,6 +1271,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       // next K read and a share of tile t's exponentiation, then the PV MFMAs
       // each followed by the next two V^T reads
       sched_step<NKB * NQC, 1, NDB * NKS, 2, (D >= 512 ? 2 : 4), kExpValuPerTile / (NKB * NQC)>();
+      if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
     };
