@@ -1284,8 +1284,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
 
     // ---- epilogue ------------------------------------------------------------
+    // O leaves through LDS up to D = 256 (below); at D = 512 one workgroup
+    // holds the CU with one wave per SIMD, nothing hides the staging's two
+    // barriers (measured 7 % slower), and a lane's fragments go straight out.
+    constexpr bool kStageO = D <= 256;
     const float l_tot = pair_sum(l_run);
-    if (!row_ok) return;
+    if constexpr (!kStageO) {
+      if (!row_ok) return;
+    }
     const bool empty = !(l_tot > 0.f);
     float inv = empty ? 0.f : fast_rcp(l_tot);
     float lse_v = empty ? -INFINITY : (m_run * sl2 + fast_log2(l_tot)) * kLn2;
@@ -1301,16 +1307,62 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         lse_v = mx + fast_log2(tot) * kLn2;
       }
     }
-    uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)qh * a.o_sh;
+    if constexpr (!kStageO) {
+      uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)qh * a.o_sh;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
-        u32x2 val = {pack_bf16(oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv),
-                     pack_bf16(oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv)};
-        if (!kPad || d0 < a.dv) *reinterpret_cast<u32x2*>(dst + d0) = val;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = 32 * (db + dh * NDB) + 8 * rr + 4 * hl;
+          u32x2 val = {pack_bf16(oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv),
+                       pack_bf16(oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv)};
+          if (!kPad || d0 < a.dv) *reinterpret_cast<u32x2*>(dst + d0) = val;
+        }
+    } else {
+      // A lane holds 4 consecutive d of one row per fragment, so direct stores
+      // would put 8 bytes in each of 32 rows per instruction (measured: the O
+      // stores then cost 3 % of the head-dim-128 prefill and 12 % of the
+      // head-dim-256 windowed one). The normalised bf16 rows are staged
+      // row-major in the tile buffers (free once every wave is past its last
+      // tile; 16-byte chunks XOR-swizzled by the row) and written back 16 bytes
+      // per lane, a row's chunks in consecutive lanes.
+      constexpr int CH = D / 8;                 // 16-byte chunks per row
+      static_assert(BM <= 4 * BN && NBUF == 2, "the staged block fits the four tile buffers");
+      auto stage = [&](int row) -> uint16_t* {
+        const int r = row % BN;
+        uint16_t* base = row < BN ? sK0 : row < 2 * BN ? sK1 : row < 3 * BN ? sV0 : sV1;
+        return base + r * D;
+      };
+      lds_barrier();                            // every wave is done reading the last tiles
+      {
+        const int srow = 32 * rg + j;
+        uint16_t* sp = stage(srow);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int c = 4 * (db + dh * NDB) + rr;   // chunk of d = 32 (db + dh NDB) + 8 rr
+            u32x2 val = {pack_bf16(oacc[db][4 * rr + 0] * inv, oacc[db][4 * rr + 1] * inv),
+                         pack_bf16(oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv)};
+            *reinterpret_cast<u32x2*>(sp + 8 * (c ^ (srow & (CH - 1))) + 4 * hl) = val;
+          }
       }
+      lds_barrier();
+      constexpr int PER = NW * 64;              // chunks per pass of the workgroup
+      static_assert((BM * CH) % PER == 0, "whole passes");
+#pragma unroll
+      for (int idx = tid; idx < BM * CH; idx += PER) {
+        const int row = idx / CH, c = idx % CH;
+        const int r = r_lo + row;
+        if (r < r_hi && (!kPad || 8 * c < a.dv)) {
+          const int qi_r = r / a.G, qh_r = g * a.G + r % a.G;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stage(row) + 8 * (c ^ (row & (CH - 1))));
+          *reinterpret_cast<u32x4*>(a.o + (int64_t)b * a.o_sb + (int64_t)qi_r * a.o_ss + (int64_t)qh_r * a.o_sh +
+                                    8 * c) = v;
+        }
+      }
+      if (!row_ok) return;
+    }
     if (a.lse != nullptr && hl == 0 && dh == 0) a.lse[((int64_t)b * a.Hq + qh) * a.Sq + qi] = lse_v;
   }
 }
