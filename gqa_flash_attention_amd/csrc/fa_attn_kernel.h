@@ -442,7 +442,6 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   int b = 0;
   int p = 0, wpmin = 0, wpmax = 0, qi = 0, qh = 0;
   bool row_ok = false;
-  bool wave_rows = false;      // this wave holds at least one row (uniform per wave)
   float slope = 0.f;           // ALiBi slope of this lane's query head (MODS)
   const uint16_t* mrow = nullptr;  // this lane's mask row (MODS with a mask)
   int mlen = 0;                // keys of the sequence (the mask is read below it)
@@ -458,7 +457,6 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const int wr_hi = min(wr_lo + 32, r_hi);
     wpmin = wr_lo / a.G + shift;
     wpmax = (wr_hi - 1) / a.G + shift;
-    wave_rows = wr_lo < r_hi;
     const int r = wr_lo + j;
     row_ok = r < r_hi;
     qi = row_ok ? r / a.G : 0;
