@@ -23,6 +23,11 @@ plus Q, O, LSE, lengths and block table) over the call's duration.
 head dims other than 64/128/256/512 and with Dk != Dv (same shapes as the
 prefill and decode workloads otherwise).
 
+The default line also carries the other prefill workloads (tiny causal,
+head dim 256 with a 1024-token window, head dim 512 causal) as keys of
+their own, each timed per call (median) after W untimed calls; they run
+before the headline.
+
 `--configs` prints one JSON line with every seeded workload timed the same
 way: the four prefill shapes (tiny causal, the headline, head dim 256 with a
 1024-token window, head dim 512 causal) in TFLOP/s and the decode and verify
@@ -249,6 +254,17 @@ def bench_configs(torch, fa, workloads, dev, steps, warmup):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(workloads, inputs_cpu):
     import numpy as np
 
@@ -259,6 +275,7 @@ def cpu_baseline(workloads, inputs_cpu):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    host_cores = len(os.sched_getaffinity(0))
     s = workloads.C2
     q, k, v = inputs_cpu
     budget_s = 12.0
@@ -278,8 +295,11 @@ def cpu_baseline(workloads, inputs_cpu):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            # threads the oracle's numpy matmuls ran on (bounded by the cores
+            # this process may use)
+            "cores": int(min(threads, host_cores)), "host_cores": host_cores, "blas_threads": int(threads),
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"all 32 query heads, {done_rows} of {s.B * s.Sq} query rows (both sequences) in "
                       f"blocks of {block} ({flops / 1e9:.1f} algorithmic GFLOP), fp64 numpy, {dt:.1f} s",
             "seconds": round(dt, 2)}
@@ -514,6 +534,22 @@ def main():
         print(json.dumps(bench_mods(torch, fa, workloads, dev, args.steps, args.warmup)), flush=True)
         return
 
+    # The other prefill workloads first (each its own leg: W untimed and K
+    # timed calls), then the headline; the decode and verify legs follow.
+    legs = {}
+    if not args.no_decode:
+        c4a, c4b = workloads.c4_inputs()
+        for s, cpu in ((workloads.C1, workloads.prefill_inputs(workloads.C1)),
+                       (workloads.C4A, c4a), (workloads.C4B, c4b)):
+            print(f"leg {s.name}", file=sys.stderr, flush=True)
+            inputs = [t.to(dev) for t in cpu]
+            legs[s.name] = bench_prefill_shape(torch, fa, dev, s, inputs, args.steps, max(args.warmup, 3))
+            if s is workloads.C1:
+                legs[s.name]["note"] = "launch-latency bound: a roofline fraction is not meaningful at 4.2 MFLOP"
+            del inputs
+            torch.cuda.empty_cache()
+        del c4a, c4b
+    print("leg prefill_c2 (headline)", file=sys.stderr, flush=True)
     pre = bench_prefill(torch, fa, workloads, dev, args.steps, args.warmup)
     src_hash = kernel_source_hash()
     traffic = read_traffic(src_hash)
@@ -543,14 +579,17 @@ def main():
         "frac_of_peak": round(pre["tflops"] / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
     }
+    line.update(legs)
     q, k, v = pre.pop("inputs")
     del q, k, v
     torch.cuda.empty_cache()
 
     if not args.no_decode:
         flush = Flusher(torch, dev)
+        print("leg decode_c3", file=sys.stderr, flush=True)
         dec = bench_decode(torch, fa, workloads, dev, workloads.C3, args.steps, args.warmup, flush)
         torch.cuda.empty_cache()
+        print("leg verify_c5", file=sys.stderr, flush=True)
         ver = bench_decode(torch, fa, workloads, dev, workloads.C5, args.steps, args.warmup, flush)
         line["decode"] = dec
         line["verify"] = ver

@@ -40,6 +40,44 @@ def _require(t, name, dtype, device=None, strided=False):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def _lse_out(lse, B, Hq, Sq, dev, return_lse=True):
+    """The caller's LSE buffer (checked) or a new one; None when not wanted."""
+    if lse is None:
+        return torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if return_lse else None
+    _require(lse, "lse", torch.float32, dev)
+    _shape(lse, "lse", (B, Hq, Sq))
+    return lse
+
+
+def _workspace(ws, need, dev):
+    """The caller's workspace (checked: a contiguous device buffer of at least
+    `need` bytes) or a new one, and its size in bytes."""
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not ws.is_cuda or ws.device != dev:
+        raise ValueError(f"workspace must be on {dev}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return ws, nbytes
+
+
+def _lengths_table(seq_lens, block_table, B, dev):
+    _require(seq_lens, "seq_lens", torch.int32, dev)
+    _shape(seq_lens, "seq_lens", (B,))
+    if block_table is not None:
+        _require(block_table, "block_table", torch.int32, dev)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [B={B}, max_pages], got {list(block_table.shape)}")
+
+
 def _strides(t):
     """(outer, token, head) element strides of a 4-D view, as a C int64[3]."""
     return (ctypes.c_int64 * 3)(*t.stride()[:3])
@@ -92,10 +130,8 @@ def prefill(q, k, v, *, causal: bool = True, window: int = 0, scale: float | Non
     if out is None:
         out = torch.empty((B, Sq, Hq, Dv), dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, dev, strided=True)
-    if out.shape != (B, Sq, Hq, Dv):
-        raise ValueError("out must be [B, Sq, Hq, Dv]")
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _shape(out, "out", (B, Sq, Hq, Dv))
+    lse = _lse_out(lse, B, Hq, Sq, dev, return_lse)
     mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, Skv, dev)
     check(load().fa_prefill_strided(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                     _ptr(out), _strides(out), _ptr(lse),
@@ -129,52 +165,46 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
     _require(q, "q", torch.bfloat16, dev, strided=True)
     _require(kcache, "kcache", torch.bfloat16, dev, strided=True)
     _require(vcache, "vcache", torch.bfloat16, dev, strided=True)
-    _require(seq_lens, "seq_lens", torch.int32, dev)
+    _lengths_table(seq_lens, block_table, B, dev)
     Dv = vcache.shape[3]
     if vcache.shape[:3] != kcache.shape[:3] or kcache.shape[3] != Dk:
         raise ValueError("kcache / vcache shapes do not match q")
     Hkv = kcache.shape[2]
-    if block_table is not None:
-        _require(block_table, "block_table", torch.int32, dev)
-        num_pages = kcache.shape[0]
-        if kcache.shape[1] != page_size:
-            raise ValueError("cache page dimension differs from page_size")
-        max_pages = block_table.shape[1]
-    else:
-        num_pages = 0
-        if kcache.shape[1] % page_size:
-            raise ValueError("contiguous cache length must be a multiple of page_size")
-        max_pages = kcache.shape[1] // page_size
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev, B, same_shape=False)
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
     need = decode_workspace_bytes(B, Sq, Hq, max(Dk, Dv), max_pages * page_size, kv_chunk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     if out is None:
         out = torch.empty((B, Sq, Hq, Dv), dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, dev, strided=True)
-    if out.shape != (B, Sq, Hq, Dv):
-        raise ValueError("out must be [B, Sq, Hq, Dv]")
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _shape(out, "out", (B, Sq, Hq, Dv))
+    lse = _lse_out(lse, B, Hq, Sq, dev, return_lse)
     mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, max_pages * page_size, dev)
     check(load().fa_decode_paged_strided(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
                                          _ptr(vcache), _strides(vcache), _ptr(block_table),
                                          _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
                                          B, Sq, Hq, Hkv, Dk, Dv, num_pages, page_size, max_pages, kv_chunk,
                                          int(bool(causal)), int(window), float(scale), mref,
-                                         _ptr(workspace), workspace.numel(), _stream(dev)))
+                                         _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse
 
 
-def _cache_geometry(kcache, vcache, block_table, page_size, dev):
-    if vcache.shape != kcache.shape:
+def _cache_geometry(kcache, vcache, block_table, page_size, dev, B, same_shape=True):
+    """(num_pages, max_pages) of a paged cache [num_pages, page_size, Hkv, D]
+    with its block table [B, max_pages], or of a contiguous cache
+    [B, Smax, Hkv, D] (num_pages 0)."""
+    if same_shape and vcache.shape != kcache.shape:
         raise ValueError("kcache and vcache differ in shape")
     if block_table is not None:
         _require(block_table, "block_table", torch.int32, dev)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [B={B}, max_pages], got {list(block_table.shape)}")
         if kcache.shape[1] != page_size:
             raise ValueError("cache page dimension differs from page_size")
         return kcache.shape[0], block_table.shape[1]
+    if kcache.shape[0] != B:
+        raise ValueError(f"a contiguous cache must be [B={B}, Smax, Hkv, D], got {list(kcache.shape)}")
     if kcache.shape[1] % page_size:
         raise ValueError("contiguous cache length must be a multiple of page_size")
     return 0, kcache.shape[1] // page_size
@@ -200,28 +230,27 @@ def decode_paged_fp8(q, kcache, vcache, k_scale, v_scale, block_table, seq_lens,
     _require(vcache, "vcache", torch.uint8, dev, strided=True)
     _require(k_scale, "k_scale", torch.float32, dev)
     _require(v_scale, "v_scale", torch.float32, dev)
-    _require(seq_lens, "seq_lens", torch.int32, dev)
+    _lengths_table(seq_lens, block_table, B, dev)
     Hkv = kcache.shape[2]
     if kcache.shape[3] != D or k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
         raise ValueError("cache head dim or scale shape does not match")
-    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev)
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev, B)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = decode_workspace_bytes(B, Sq, Hq, D, max_pages * page_size, kv_chunk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, dev, strided=True)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _shape(out, "out", (B, Sq, Hq, D))
+    lse = _lse_out(lse, B, Hq, Sq, dev, return_lse)
     mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, max_pages * page_size, dev)
     check(load().fa_decode_paged_fp8(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
                                      _ptr(vcache), _strides(vcache), _ptr(k_scale), _ptr(v_scale),
                                      _ptr(block_table), _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
                                      B, Sq, Hq, Hkv, D, num_pages, page_size, max_pages, kv_chunk,
                                      int(bool(causal)), int(window), float(scale), mref,
-                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+                                     _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse
 
 
@@ -238,10 +267,12 @@ def kv_append_fp8(kcache, vcache, k_scale, v_scale, block_table, seq_lens, knew,
         _require(t, n, torch.uint8, dev, strided=True)
     _require(k_scale, "k_scale", torch.float32, dev)
     _require(v_scale, "v_scale", torch.float32, dev)
-    _require(seq_lens, "seq_lens", torch.int32, dev)
+    _lengths_table(seq_lens, block_table, B, dev)
     if vnew.shape != knew.shape or kcache.shape[2:] != (Hkv, D):
         raise ValueError("shape mismatch between caches and new rows")
-    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev)
+    if k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("k_scale and v_scale must be [Hkv]")
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev, B)
     check(load().fa_kv_append_fp8(_ptr(kcache), _strides(kcache), _ptr(vcache), _strides(vcache),
                                   _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
                                   _ptr(knew), _strides(knew), _ptr(vnew), _strides(vnew),
@@ -254,12 +285,15 @@ def combine_lse(o_part, lse_part, n_chunks=None, *, out=None, lse=None):
     dev = o_part.device
     _require(o_part, "o_part", torch.float32, dev)
     _require(lse_part, "lse_part", torch.float32, dev)
+    _shape(lse_part, "lse_part", (B, Hq, Sq, C))
     if n_chunks is not None:
         _require(n_chunks, "n_chunks", torch.int32, dev)
+        _shape(n_chunks, "n_chunks", (B,))
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    _shape(out, "out", (B, Sq, Hq, D))
+    lse = _lse_out(lse, B, Hq, Sq, dev)
     check(load().fa_combine_lse(_ptr(o_part), _ptr(lse_part), _ptr(n_chunks), C, _ptr(out),
                                 _ptr(lse), B, Sq, Hq, D, _stream(dev)))
     return out, lse
@@ -278,19 +312,11 @@ def kv_append(kcache, vcache, block_table, seq_lens, knew, vnew, *, page_size: i
     dev = knew.device
     for t, n in ((kcache, "kcache"), (vcache, "vcache"), (knew, "knew"), (vnew, "vnew")):
         _require(t, n, torch.bfloat16, dev, strided=True)
-    _require(seq_lens, "seq_lens", torch.int32, dev)
+    _lengths_table(seq_lens, block_table, B, dev)
     if (vnew.shape[:3] != knew.shape[:3] or vcache.shape[:3] != kcache.shape[:3]
             or kcache.shape[2:] != (Hkv, Dk) or vcache.shape[3] != Dv):
         raise ValueError("shape mismatch between caches and new rows")
-    if block_table is not None:
-        _require(block_table, "block_table", torch.int32, dev)
-        if kcache.shape[1] != page_size:
-            raise ValueError("cache page dimension differs from page_size")
-        num_pages, max_pages = kcache.shape[0], block_table.shape[1]
-    else:
-        if kcache.shape[1] % page_size:
-            raise ValueError("contiguous cache length must be a multiple of page_size")
-        num_pages, max_pages = 0, kcache.shape[1] // page_size
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev, B, same_shape=False)
     check(load().fa_kv_append(_ptr(kcache), _strides(kcache), _ptr(vcache), _strides(vcache),
                               _ptr(block_table), _ptr(seq_lens), _ptr(knew), _strides(knew),
                               _ptr(vnew), _strides(vnew), B, Snew, Hkv, Dk, Dv, num_pages, page_size,
@@ -303,10 +329,11 @@ def paged_gather(cache, block_table, seq_lens, *, out=None):
     B, max_pages = block_table.shape
     dev = cache.device
     _require(cache, "cache", torch.bfloat16, dev)
-    _require(block_table, "block_table", torch.int32, dev)
-    _require(seq_lens, "seq_lens", torch.int32, dev)
+    _lengths_table(seq_lens, block_table, B, dev)
     if out is None:
         out = torch.empty((B, max_pages * ps, Hkv, D), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    _shape(out, "out", (B, max_pages * ps, Hkv, D))
     check(load().fa_paged_gather(_ptr(cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
                                  B, Hkv, D, P, ps, max_pages, _stream(dev)))
     return out

@@ -11,9 +11,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# GQAFA_LIBRARY may name another build of the same library (same C ABI), e.g.
-# a build with different tile parameters; by default the in-tree build loads.
-LIB_PATH = os.environ.get("GQAFA_LIBRARY") or os.path.join(_HERE, "libgqafa.so")
+# Always the in-tree build (no other library is ever loaded in its place).
+LIB_PATH = os.path.join(_HERE, "libgqafa.so")
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED",

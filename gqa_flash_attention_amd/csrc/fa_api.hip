@@ -144,7 +144,8 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
-  if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0) return 0;
+  if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0 || kv_chunk % 32 != 0)
+    return 0;
   const int64_t slots = n_chunks_for(max_seq_len, kv_chunk) + 1;
   const int64_t rows = (int64_t)B * Hq * Sq;
   const int64_t width = tile_dim(D, D);     // partials are as wide as the tile
@@ -173,7 +174,8 @@ int decode_impl(const void* q, const int64_t* q_stride,
   if (kv8 && (Dk != 128 || Dv != 128)) return FA_ERR_UNSUPPORTED;
   Mods md;
   if (!get_mods(mods, md)) return FA_ERR_INVALID_ARG;
-  if (max_pages_per_seq < 0 || kv_chunk <= 0) return FA_ERR_INVALID_ARG;
+  // chunks are whole 32-key tiles
+  if (max_pages_per_seq < 0 || kv_chunk <= 0 || kv_chunk % 32 != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
@@ -230,7 +232,7 @@ int decode_impl(const void* q, const int64_t* q_stride,
     const int s = to_status(launch_split(sd, st));
     if (s != FA_OK) return s;
   }
-  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, kv_chunk, (int)n_slots, o, lse, os, md.sinks,
+  CombineDesc cd{o_part, lse_part, nullptr, seq_lens, (int)max_len, kv_chunk, (int)n_slots, o, lse, os, md.sinks,
                  B, Sq, Hq, D, Dv};
   return to_status(launch_combine(cd, st));
 }
@@ -294,7 +296,7 @@ int fa_combine_lse(const float* o_part, const float* lse_part, const int32_t* n_
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Sq > kMaxGrid) return FA_ERR_INVALID_ARG;
   const Strides od{(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
-  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, max_chunks, o, lse, od, nullptr, B, Sq, Hq, D, D};
+  CombineDesc cd{o_part, lse_part, n_chunks, nullptr, 0, 0, max_chunks, o, lse, od, nullptr, B, Sq, Hq, D, D};
   return to_status(launch_combine(cd, static_cast<hipStream_t>(stream)));
 }
 

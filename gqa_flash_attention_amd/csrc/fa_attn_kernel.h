@@ -342,10 +342,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   auto stage_table = [&](int b_t, int pf) {
     lds_barrier();                          // every wave is done with the old window
     const int np = min(TAB, a.max_pages - pf);
-    for (int i = tid; i < np; i += NW * 64) {
-      const int page = a.table[(int64_t)b_t * a.max_pages + pf + i];
-      sT[i] = min(max(page, 0), a.num_pages - 1);
-    }
+    for (int i = tid; i < np; i += NW * 64) sT[i] = clamp_page(a.table[(int64_t)b_t * a.max_pages + pf + i], a.num_pages);
     lds_barrier();
     tw_b = b_t;
     tw_p0 = pf;
@@ -377,10 +374,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         const int p0 = __builtin_amdgcn_readfirstlane(sT[(tb >> a.page_shift) - tw_p0]);
         const int p1 = __builtin_amdgcn_readfirstlane(sT[((tb + 16) >> a.page_shift) - tw_p0]);
         const int64_t sb = is_v ? a.v_sb : a.k_sb;
-        const char* base0 = reinterpret_cast<const char*>(kv_base) +
-                            ES * ((int64_t)p0 * sb + (int64_t)(tb & mask) * rs);
+        const char* base0 = reinterpret_cast<const char*>(kv_base) + ES * paged_row(p0, tb & mask, sb, rs);
         const char* base1 = reinterpret_cast<const char*>(kv_base) +
-                            ES * ((int64_t)p1 * sb + (int64_t)((tb + 16) & mask) * rs - 16 * (int64_t)rs);
+                            ES * (paged_row(p1, (tb + 16) & mask, sb, rs) - 16 * (int64_t)rs);
 #pragma unroll
         for (int i = 0; i < SEGW; ++i) {
           const int row = KEEP_SEG ? srow[i] : seg_row(i);
@@ -400,13 +396,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         const int t = tb + min(row, lim);
         int page;
         if constexpr (TAB > 0) {
-          page = sT[(t >> a.page_shift) - tw_p0];
+          page = sT[(t >> a.page_shift) - tw_p0];     // clamped when staged
         } else {
-          page = a.table[(int64_t)b_t * a.max_pages + (t >> a.page_shift)];
-          page = min(max(page, 0), a.num_pages - 1);
+          page = clamp_page(a.table[(int64_t)b_t * a.max_pages + (t >> a.page_shift)], a.num_pages);
         }
-        const int64_t base = (int64_t)page * (is_v ? a.v_sb : a.k_sb) +
-                             (int64_t)((t & ((1 << a.page_shift) - 1)) - row) * rs;
+        // the lane's offset inside the tile (off0) already holds row * rs,
+        // so the slot passed here is the token's slot minus the row
+        const int64_t base = paged_row(page, (t & ((1 << a.page_shift) - 1)) - row, is_v ? a.v_sb : a.k_sb, rs);
         src = reinterpret_cast<const char*>(kv_base) + ES * base + off0;
       } else {
         // uniform tile base + 32-bit per-lane byte offset

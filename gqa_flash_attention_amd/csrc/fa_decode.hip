@@ -1,5 +1,6 @@
 // Split-KV dispatch by head dim, the LSE combine kernel and the paged-gather
-// test hook.
+// test hook (which applies the split kernel's page address rule, clamp_page
+// and paged_row of fa_device.h, to every token).
 //
 // Split-KV (fa_split.h): a persistent grid streams all K/V tiles in equal
 // contiguous ranges and writes one fp32 partial output per range and block
@@ -21,6 +22,7 @@ struct CombineArgs {
   const float* lse_part;
   const int32_t* n_chunks;
   const int32_t* seq_lens;
+  int max_len;
   int kv_chunk, n_slots;
   uint16_t* o;
   float* lse;
@@ -69,7 +71,8 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
   if (c.n_chunks != nullptr) {
     n = c.n_chunks[b];
   } else if (c.seq_lens != nullptr) {
-    const int len = max(c.seq_lens[b], 0);
+    // the split kernel clamps lengths into the cache the same way
+    const int len = min(max(c.seq_lens[b], 0), c.max_len);
     n = len > 0 ? (int)(((int64_t)len + c.kv_chunk - 1) / c.kv_chunk) + 1 : 0;
   }
   n = max(0, min(n, c.n_slots));
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
 
 template <int D>
 hipError_t run_combine(const CombineDesc& d, hipStream_t stream) {
-  CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.kv_chunk, d.n_slots,
+  CombineArgs c{d.o_part, d.lse_part, d.n_chunks, d.seq_lens, d.max_len, d.kv_chunk, d.n_slots,
                 static_cast<uint16_t*>(d.o), d.lse, d.os.outer, d.os.token, d.os.head, d.sinks,
                 d.dv, d.B, d.Sq, d.Hq};
   const int64_t rows = (int64_t)d.B * d.Hq * d.Sq;
@@ -187,7 +190,8 @@ struct GatherArgs {
   int B, Hkv, D, num_pages, page_shift, max_pages;
 };
 
-// One thread per 16-byte chunk of the dense output; grid-stride.
+// One thread per 16-byte chunk of the dense output; grid-stride. Slots at or
+// past a sequence's length are written as zero.
 __global__ void __launch_bounds__(256) gather_kernel(const GatherArgs a) {
   const int64_t slots = (int64_t)a.max_pages << a.page_shift;
   const int chunks = a.D / 8;
@@ -200,17 +204,15 @@ __global__ void __launch_bounds__(256) gather_kernel(const GatherArgs a) {
     rest /= a.Hkv;
     const int t = (int)(rest % slots);
     const int b = (int)(rest / slots);
-    KvAddr kv;
-    kv.table = a.table;
-    kv.page_shift = a.page_shift;
-    kv.max_pages = a.max_pages;
-    kv.num_pages = a.num_pages;
-    kv.slots = slots;
-    kv.row_stride = (int64_t)a.Hkv * a.D;
-    kv.head_off = (int64_t)g * a.D;
     int64_t len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > slots ? slots : len);
-    const int64_t off = t < len ? kv.row(b, t) : -1;
+    // the split kernel's address rule: clamped page, then slot
+    const int64_t off = t < len ? paged_row(clamp_page(a.table[(int64_t)b * a.max_pages + (t >> a.page_shift)],
+                                                       a.num_pages),
+                                            t & ((1 << a.page_shift) - 1),
+                                            ((int64_t)a.Hkv * a.D) << a.page_shift, (int64_t)a.Hkv * a.D) +
+                                      (int64_t)g * a.D
+                                : -1;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (off >= 0) w = *reinterpret_cast<const u32x4*>(a.cache + off + 8 * ch);
     *reinterpret_cast<u32x4*>(a.out + (((int64_t)b * slots + t) * a.Hkv + g) * a.D + 8 * ch) = w;

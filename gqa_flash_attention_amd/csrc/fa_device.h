@@ -1,6 +1,7 @@
 // Device helpers for the gfx950 (CDNA4) attention kernels: MFMA operand
-// types, lane exchanges, bf16 packing, LDS swizzles and the KV-cache address
-// function shared by the split-KV kernel and the paged-gather test hook.
+// types, lane exchanges, bf16 packing, LDS reads and copies, and the paged
+// KV-cache address rule shared by the split-KV kernel and the paged-gather
+// test hook.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -193,27 +194,18 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
   return r;
 }
 
-// Element offset of K/V row (sequence b, token t, KV head g) in a cache laid
-// out as pages [num_pages, page_size, Hkv, D] reached through block_table
-// [B, max_pages], or, with no table, as a contiguous [B, slots, Hkv, D]
-// tensor (the identity table). Returns -1 when the table entry is outside
-// [0, num_pages). All arithmetic is 64-bit.
-struct KvAddr {
-  const int32_t* table;   // may be null
-  int page_shift;         // log2(page_size)
-  int max_pages;          // table row length
-  int num_pages;
-  int64_t slots;          // contiguous layout: token slots per sequence
-  int64_t row_stride;     // Hkv * D elements between consecutive tokens
-  int64_t head_off;       // g * D
+// Paged KV caches [num_pages, page_size, Hkv, D]: the address rule of the
+// split-KV kernel, shared with the paged-gather hook (fa_paged_gather), so
+// that the hook's byte-exact test pins the decode path's own arithmetic.
+// A block-table entry outside [0, num_pages) is clamped into range (every
+// load stays inside the cache; a sequence with such an entry covering its
+// tokens gets unspecified output).
+__device__ __forceinline__ int clamp_page(int page, int num_pages) { return min(max(page, 0), num_pages - 1); }
 
-  __device__ __forceinline__ int64_t row(int b, int t) const {
-    if (table == nullptr) return ((int64_t)b * slots + t) * row_stride + head_off;
-    const int page = table[(int64_t)b * max_pages + (t >> page_shift)];
-    if (page < 0 || page >= num_pages) return -1;
-    const int slot = t & ((1 << page_shift) - 1);
-    return (((int64_t)page << page_shift) + slot) * row_stride + head_off;
-  }
-};
+// Element offset of slot `slot` of (clamped) page `page`, given the page and
+// token strides of the cache (head offset not included). 64-bit arithmetic.
+__device__ __forceinline__ int64_t paged_row(int page, int slot, int64_t page_stride, int64_t token_stride) {
+  return (int64_t)page * page_stride + (int64_t)slot * token_stride;
+}
 
 }  // namespace gqafa

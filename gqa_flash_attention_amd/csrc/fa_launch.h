@@ -43,7 +43,9 @@ struct SplitDesc {
 struct CombineDesc {
   const float* o_part; const float* lse_part;
   const int32_t* n_chunks;   // device [B] or null: partials to merge per sequence
-  const int32_t* seq_lens;   // used when n_chunks is null: ceil(len / kv_chunk) + 1 slots (0 if len = 0)
+  const int32_t* seq_lens;   // used when n_chunks is null: ceil(len / kv_chunk) + 1 slots (0 if len = 0),
+                             // len = seq_lens[b] clamped to [0, max_len]
+  int max_len;               // keys a sequence can hold (the cache's capacity)
   int kv_chunk, n_slots;     // n_slots: slots per row in memory
   void* o; float* lse;
   Strides os;                // o [B, Sq, Hq, D]

@@ -13,8 +13,12 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned, owned by the
- *     caller. The library never allocates, frees or synchronizes, and keeps
- *     no state between calls.
+ *     caller. The library never allocates, frees or synchronizes. Its only
+ *     process state is a per-(kernel, device) count of the workgroups a
+ *     device holds at once (the split-KV kernels' grid size), computed on a
+ *     device's first decode call from the runtime's occupancy query; it is a
+ *     pure function of the kernel and the device, so no result depends on
+ *     call history.
  *   - bf16 tensors are passed as raw 16-bit storage (bfloat16 bit patterns).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     default stream). Results are ready when the stream reaches the call.
@@ -45,7 +49,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad mask or scale, misaligned pointer */
-  FA_ERR_UNSUPPORTED = -2,  /* head dim not in {64,128,256,512}, page size not a power of two */
+  FA_ERR_UNSUPPORTED = -2,  /* head dim not a multiple of 8 in [8, 512], page size not a power of two */
   FA_ERR_WORKSPACE = -3,    /* decode workspace missing or smaller than fa_decode_workspace_bytes */
   FA_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch */
 } fa_status;
@@ -168,7 +172,9 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
  *               unspecified. Entries past a sequence's last page are never
  *               used.
  *   page_size   a power of two in [1, 65536]
- *   kv_chunk    tokens per chunk, > 0 (a multiple of 32 keeps every tile whole)
+ *   kv_chunk    tokens per chunk, a positive multiple of 32 (the split's
+ *               32-key tiles never straddle a chunk); FA_ERR_INVALID_ARG
+ *               otherwise
  *   workspace   device buffer of at least
  *               fa_decode_workspace_bytes(B, Sq, Hq, D, max_pages_per_seq*page_size, kv_chunk)
  *
@@ -248,7 +254,10 @@ int fa_decode_paged_fp8(const void* q, const int64_t* q_stride,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Merge split-KV partials by their LSE:
+ * Merge split-KV partials by their LSE (the combine step that runs after the
+ * split blocks on the same stream when a KV range is cut into parallel
+ * blocks: beellama.cpp PR 149, first review; every partial publishes its
+ * row max and sum as an LSE, same page, Overview):
  *   M = max_c LSE_c,  LSE = M + ln sum_c exp(LSE_c - M),
  *   O = sum_c exp(LSE_c - LSE) * O_c.
  * Chunks with LSE_c = -inf have weight 0; a row whose chunks are all empty
@@ -321,11 +330,18 @@ int fa_kv_append_fp8(void* kcache, const int64_t* k_stride, void* vcache, const 
 const char* fa_status_string(int status);
 
 /*
- * Test hook: gathers a paged cache into a dense tensor with the same device
- * address function the decode kernel uses.
+ * Test hook: gathers a paged cache into a dense tensor through the split-KV
+ * kernel's own page address rule (clamp_page and paged_row in the library's
+ * device header: a table entry is clamped into [0, num_pages), then token t
+ * is slot t % page_size of that page), so that a byte-exact comparison with
+ * a CPU gather pins the decode path's address arithmetic (vLLM PR 32,
+ * Validation: the paged indexer's picks are checked for identity against a
+ * reference).
  *   cache [num_pages, page_size, Hkv, D] bf16 -> out [B, max_pages_per_seq*page_size, Hkv, D]
- * Slots at or beyond seq_lens[b], and slots whose table entry is outside
- * [0, num_pages), are written as zero.
+ *   seq_lens int32 [B] on the device, clamped to [0, max_pages_per_seq*page_size]
+ * Slots at or beyond seq_lens[b] are written as zero; a slot whose table
+ * entry is outside [0, num_pages) holds the row of the page the entry clamps
+ * to, as the decode kernel reads it.
  */
 int fa_paged_gather(const void* cache, const int32_t* block_table, const int32_t* seq_lens,
                     void* out, int B, int Hkv, int D, int num_pages, int page_size,

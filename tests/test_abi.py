@@ -93,6 +93,7 @@ def _decode(lib, **kw):
     (dict(D=520), UNSUPPORTED), (dict(D=100), UNSUPPORTED), (dict(page_size=12), UNSUPPORTED),
     (dict(page_size=0), UNSUPPORTED), (dict(page_size=1 << 17), UNSUPPORTED), (dict(D=80, B=0), OK),
     (dict(Hq=7), INVALID), (dict(chunk=0), INVALID), (dict(max_pages=-1), INVALID),
+    (dict(chunk=48), INVALID), (dict(chunk=100), INVALID), (dict(chunk=33), INVALID),
     (dict(window=3, causal=0), INVALID), (dict(scale=0.0), INVALID),
     (dict(num_pages=0), INVALID), (dict(lens=None), INVALID), (dict(q=None), INVALID),
     (dict(k=P + 4), INVALID),
@@ -110,9 +111,10 @@ def test_workspace_bytes(lib):
     assert f(16, 1, 32, 128, 16384, 256) == 16 * 32 * 65 * 128 * 4 + 16 * 32 * 65 * 4
     assert f(1, 1, 1, 100, 10, 4) == 0         # unsupported head dim
     assert f(1, 1, 1, 64, 10, 0) == 0          # bad chunk
+    assert f(1, 1, 1, 64, 10, 48) == 0         # chunks are whole 32-key tiles
     # head dims below a tile width are sized at the tile width
     assert f(16, 1, 32, 80, 16384, 256) == f(16, 1, 32, 128, 16384, 256)
-    assert f(2, 3, 4, 320, 1000, 100) == f(2, 3, 4, 512, 1000, 100)
+    assert f(2, 3, 4, 320, 1000, 96) == f(2, 3, 4, 512, 1000, 96)
 
 
 def test_workspace_bytes_alignment(lib):
@@ -121,7 +123,7 @@ def test_workspace_bytes_alignment(lib):
     o = rows * slots * D * 4
     l = rows * slots * 4
     up = lambda x: (x + 255) // 256 * 256
-    assert f(1, 3, 2, 64, 10, 4) == up(o) + up(l)
+    assert f(1, 3, 2, 64, 70, 32) == up(o) + up(l)
 
 
 @pytest.mark.parametrize("kw,want", [

@@ -83,7 +83,7 @@ def test_paged_gather_bitexact():
     P, ps, Hkv, D, B, mp = 97, 16, 3, 64, 4, 20
     cache = torch.randn(P, ps, Hkv, D, generator=gen).to(torch.bfloat16)
     table = torch.randint(0, P, (B, mp), generator=gen, dtype=torch.int32)
-    table[1, 3] = P + 5          # out-of-range entries read as zero
+    table[1, 3] = P + 5          # out-of-range entries read the page they clamp to
     table[2, 0] = -1
     lens = torch.tensor([320, 60, 1, 0], dtype=torch.int32)
     out = fa.paged_gather(cache.to(DEV), table.to(DEV), lens.to(DEV))
@@ -91,9 +91,8 @@ def test_paged_gather_bitexact():
     ref = torch.zeros(B, mp * ps, Hkv, D, dtype=torch.bfloat16)
     for b in range(B):
         for t in range(int(lens[b])):
-            pg = int(table[b, t // ps])
-            if 0 <= pg < P:
-                ref[b, t] = cache[pg, t % ps]
+            pg = min(max(int(table[b, t // ps]), 0), P - 1)
+            ref[b, t] = cache[pg, t % ps]
     assert torch.equal(out.cpu().view(torch.int16), ref.view(torch.int16))
     # the oracle's gather agrees where every table entry is valid
     valid = table.clone()
@@ -102,6 +101,37 @@ def test_paged_gather_bitexact():
     g2 = fa.paged_gather(cache.to(DEV), valid.to(DEV), lens.to(DEV)).cpu()
     r2 = oracle.paged_gather_ref(cache, valid, lens, ps, mp * ps)
     assert torch.equal(g2.view(torch.int16), r2.view(torch.int16))
+
+
+def test_out_of_range_table_entry_is_clamped():
+    """A block-table entry outside [0, num_pages) is clamped into range by the
+    decode kernel (the rule the gather hook shares): the call equals the
+    same call over the clamped table, bit for bit, and reads nothing out of
+    bounds."""
+    shape = workloads.DecodeShape("clamp", B=3, Sq=8, Hq=16, Hkv=2, D=128, page_size=16, max_len=1024,
+                                  len_lo=600, len_hi=1024, kv_chunk=256, seed=23)
+    di = workloads.decode_inputs(shape)
+    P = di.kcache.shape[0]
+    bad = di.block_table.clone()
+    bad[0, 2] = P + 7
+    bad[1, 0] = -3
+    bad[2, 5] = 1 << 30
+    clamped = bad.clamp(0, P - 1)
+    o1, l1 = _decode(workloads.DecodeInputs(di.q, di.kcache, di.vcache, bad, di.seq_lens), shape)
+    o2, l2 = _decode(workloads.DecodeInputs(di.q, di.kcache, di.vcache, clamped, di.seq_lens), shape)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_combine_caps_lengths_at_the_cache():
+    """seq_lens beyond the cache's capacity are clamped to it, also when the
+    capacity is zero: rows of an empty cache get O = 0 and LSE = -inf."""
+    B, Sq, Hq, Hkv, D = 2, 1, 8, 2, 64
+    q = torch.randn(B, Sq, Hq, D).to(torch.bfloat16).to(DEV)
+    kc = torch.zeros(B, 0, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    lens = torch.tensor([5, 300], dtype=torch.int32, device=DEV)
+    o, lse = fa.decode_paged(q, kc, kc, None, lens, page_size=16, kv_chunk=64)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
 
 
 COMBINE_CASES = [(D, 7, (7, 5, 0)) for D in (64, 128, 256, 512)] + [

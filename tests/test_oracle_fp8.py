@@ -1,7 +1,8 @@
 """Pins of the oracle's fp8 (OCP e4m3) KV encoding (CPU): values the format's
 definition fixes, torch's float8_e4m3fn dtype as an independent library
 decoder and encoder, exact round trips, ties to even at midpoints,
-saturation, and the fp8 append's index map against a loop over tokens."""
+saturation, the per-head dequantisation against torch's decoder times a
+scale per head, and the fp8 append's index map against a loop over tokens."""
 
 import math
 
@@ -95,8 +96,33 @@ def check_fp8_append_index_map(orc):
     assert not np.array_equal(k2, kc)
 
 
+def check_dequantize_per_head(orc):
+    """The cached value of a byte of KV head g is e4m3(byte) * scale[g]:
+    torch's float8_e4m3fn decoder widened to fp64 times a distinct scale per
+    head, on a paged-cache-shaped array [P, 16, Hkv, D] with Hkv != D (so a
+    scale broadcast along D, or one head's scale for all, differs)."""
+    rng = np.random.default_rng(5)
+    P, ps, Hkv, D = 3, 16, 3, 8
+    codes = rng.integers(0, 256, (P, ps, Hkv, D)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E                  # keep the comparison finite
+    codes[codes == 0xFF] = 0xFE
+    scale = np.array([0.25, 3.0, 1.0 / 7.0], dtype=np.float32)
+    got = orc.dequantize_e4m3(codes, scale)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = np.empty_like(dec)
+    for g in range(Hkv):
+        want[:, :, g, :] = dec[:, :, g, :] * float(scale[g])
+    assert got.shape == codes.shape
+    assert np.array_equal(got, want)
+    # a NaN code stays NaN (and only there)
+    nan_codes = codes.copy()
+    nan_codes[0, 0, 1, 2] = 0x7F
+    out = orc.dequantize_e4m3(nan_codes, scale)
+    assert np.isnan(out[0, 0, 1, 2]) and np.isnan(out).sum() == 1
+
+
 FP8_CHECKS = [check_e4m3_spot_values, check_e4m3_against_torch_dtype, check_quantize_round_trip_ties_saturation,
-              check_fp8_append_index_map]
+              check_fp8_append_index_map, check_dequantize_per_head]
 
 
 def test_e4m3_spot_values():
@@ -113,3 +139,7 @@ def test_quantize_round_trip_ties_saturation():
 
 def test_fp8_append_index_map():
     check_fp8_append_index_map(oracle)
+
+
+def test_dequantize_per_head():
+    check_dequantize_per_head(oracle)

@@ -86,6 +86,9 @@ FP8_MUTATIONS = {
     "sign dropped": ("codes | 0x80", "codes"),
     "append token off by one": ("            t = n - snew + i\n", "            t = n - snew + i + 1\n"),
     "append ignores the head scale": ("kq = quantize_e4m3(kn / ks[None, None, :, None])", "kq = quantize_e4m3(kn / ks[0])"),
+    "dequantise with head 0's scale for every head": ("return vals * scale[:, None]", "return vals * scale[0]"),
+    "dequantise with the scale broadcast along D": ("return vals * scale[:, None]",
+                                                   "return vals * np.resize(scale, vals.shape[-1])"),
 }
 
 
