@@ -324,6 +324,30 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       voff[i] = seg_voff(i);
     }
   }
+  // Prefill copy geometry: a 1 KiB segment covers RPS = 64 / KCH key rows;
+  // lane L fetches row p_lr = L / KCH of its segment into physical chunk
+  // L % KCH, i.e. logical chunk (L % KCH) ^ swizzle(row). Since RPS is a
+  // power of two and p_lr < RPS, both swizzles of row sg RPS + p_lr split
+  // into a per-lane part and a per-segment (uniform) part.
+  constexpr int RPS = 64 / KCH;
+  const int p_lr = lane / KCH, p_pc = lane % KCH;
+  const uint32_t p_lrk = (uint32_t)(p_lr * ES * k_rs);
+  const uint32_t p_lrv = (uint32_t)(p_lr * ES * v_rs);
+  // K: swz_k(sg RPS + lr) = swz_k-bits of (sg RPS) ^ those of lr (disjoint)
+  const int p_kx = D >= 128 ? (p_pc ^ p_lr) : (p_pc ^ (p_lr >> 1));
+  auto p_kchunk = [&](int sg) -> int {
+    const int c = D >= 128 ? ((sg * RPS) & 15) : ((sg * 4) & 7);
+    return p_kx ^ c;
+  };
+  // V: swz_v depends on row & 3 only
+  const int p_vx0 = p_pc ^ swz_v<D>(p_lr & 3);
+  const int p_vx1 = p_pc ^ swz_v<D>((2 + p_lr) & 3);
+  auto p_vchunk = [&](int sg) -> int {
+    if constexpr (RPS == 1) return lane ^ swz_v<D>(sg & 3);
+    else if constexpr (RPS == 2) return (sg & 1) ? p_vx1 : p_vx0;
+    else return p_vx0;
+  };
+
   // Head dims below D: the byte distance from this lane's chunk of segment i
   // back to chunk 0 of its key row when the chunk lies past the real K or V
   // head dim, else 0 (recomputed at each copy of a padded call: a few integer
@@ -359,6 +383,36 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const int lim = ke_t - 1 - tb;            // last valid row of this tile
     const bool tail = lim < BN - 1;           // uniform
     const int rs = is_v ? v_rs : k_rs;
+    if constexpr (!SPLIT) {
+      // Prefill (dense K/V), buffer form: segment sg holds rows sg RPS ..
+      // sg RPS + RPS - 1 of the tile; this lane fetches logical chunk lc of
+      // row sg RPS + p_lr. The row part of the source offset is uniform
+      // (soffset); the lane part is one per-lane constant plus the chunk.
+      // (A few registers instead of three per segment: at head dim 512 the
+      // per-segment offsets left the main loop too few registers to keep
+      // more than one LDS operand read in flight.)
+      const int rsb = ES * rs;                          // bytes per key row
+      const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
+      const uint32_t lro = is_v ? p_lrv : p_lrk;        // p_lr * rsb
+#pragma unroll
+      for (int i = 0; i < SEGW; ++i) {
+        const int sg = wave * SEGW + i;                 // uniform
+        const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
+        uint32_t o = lro + 16u * (uint32_t)lc;
+        if (tail) {
+          // rows past the last valid one read that row instead (their scores
+          // are masked, their V rows get weight 0)
+          const int r = sg * RPS + p_lr;
+          if (r > lim) o -= (uint32_t)((r - lim) * rsb);
+        }
+        if constexpr (kPad) {
+          // a chunk past the real head dim reads chunk 0 of the same row
+          if (8 * lc >= (is_v ? a.dv : a.dk)) o -= 16u * (uint32_t)lc;
+        }
+        dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
+      }
+      return;
+    }
     if constexpr (PAGED && TAB > 0) {
       const int pf = tb >> a.page_shift, pl = (tb + min(lim, BN - 1)) >> a.page_shift;
       if (b_t != tw_b || pf < tw_p0 || pl >= tw_p0 + TAB) stage_table(b_t, pf);
@@ -1256,15 +1310,92 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       // arbiter feeds the matrix cores first (measured +2.4 % at head dim
       // 128; with one workgroup per CU it gains nothing).
       if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(1);
-      scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
-      u32x4 pf[NKS];
-      exponentiate(sc, nb, pf);
-      publish(sn, (it + 1) & 1);
-      accumulate(vbuf(u), pf);
-      // one schedule for the whole step: S(t+1) MFMAs each followed by the
-      // next K read and a share of tile t's exponentiation, then the PV MFMAs
-      // each followed by the next two V^T reads
-      sched_step<NKB * NQC, 1, NDB * NKS, 2, (D >= 512 ? 2 : 4), kExpValuPerTile / (NKB * NQC)>();
+      if constexpr (D >= 512) {
+        // Head dim 512 runs one wave per SIMD, so nothing covers a wave's
+        // own LDS latency, and its registers are too full for the compiler
+        // to keep more than one operand read in flight on its own. The step
+        // is written in explicit batches instead: the reads of the next
+        // batch are issued before the MFMAs of the current one (a schedule
+        // fence between batches), and tile t's exponentiation is spread
+        // over the S(t+1) batches.
+        const uint16_t* bk = kbuf((u + 1) % NBUF);
+        const uint16_t* bv = vbuf(u);
+        constexpr int KB = 4;                    // MFMAs per batch
+        constexpr int NSB = NQC / KB;            // S batches
+        constexpr int NPAIR = NKS * 4;           // exponentiated pairs per lane
+        static_assert(NKB == 1 && NQC % KB == 0 && (NKS * NDB) % KB == 0, "head dim 512 tile shape");
+        auto kread = [&](int c) -> u32x4 {
+          const int ch = 2 * (c + dh * NQC) + hl;
+          return *reinterpret_cast<const u32x4*>(&bk[j * D + 8 * (ch ^ swz_k<D>(j))]);
+        };
+        u32x4 kf[2][KB];
+#pragma unroll
+        for (int x = 0; x < KB; ++x) kf[0][x] = kread(x);
+        sn[0] = f32x16{};
+        u32x4 pf[NKS];
+        float ls = 0.f;
+#pragma unroll
+        for (int bi = 0; bi < NSB; ++bi) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (bi + 1 < NSB) {
+#pragma unroll
+            for (int x = 0; x < KB; ++x) kf[(bi + 1) & 1][x] = kread((bi + 1) * KB + x);
+          }
+#pragma unroll
+          for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
+          // pairs q with q * NSB / NPAIR == bi: an even share per batch
+#pragma unroll
+          for (int q = 0; q < NPAIR; ++q) {
+            if (q * NSB / NPAIR != bi) continue;
+            const int ks = q / 4, w = q % 4, base = 8 * (ks & 1);
+            const float e0 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w], sl2, nb));
+            const float e1 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w + 1], sl2, nb));
+            ls += e0 + e1;
+            pf[ks][w] = pack_bf16(e0, e1);
+          }
+        }
+        l_run += ls;
+        __builtin_amdgcn_sched_barrier(0);
+        publish(sn, (it + 1) & 1);
+        // O^T += V^T P^T in batches of KB MFMAs, two transposing reads each
+        constexpr int NPV = NKS * NDB;
+        auto vread = [&](int m, u32x4& out) {
+          const int ks = m / NDB, db = m % NDB;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
+            out[2 * half] = t[0];
+            out[2 * half + 1] = t[1];
+          }
+        };
+        u32x4 vf[2][KB];
+#pragma unroll
+        for (int x = 0; x < KB; ++x) vread(x, vf[0][x]);
+#pragma unroll
+        for (int bi = 0; bi < NPV / KB; ++bi) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (bi + 1 < NPV / KB) {
+#pragma unroll
+            for (int x = 0; x < KB; ++x) vread((bi + 1) * KB + x, vf[(bi + 1) & 1][x]);
+          }
+#pragma unroll
+          for (int x = 0; x < KB; ++x) {
+            const int m = bi * KB + x, ks = m / NDB, db = m % NDB;
+            oacc[db] = mfma32(as_bf16x8(vf[bi & 1][x]), as_bf16x8(pf[ks]), oacc[db]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
+        u32x4 pf[NKS];
+        exponentiate(sc, nb, pf);
+        publish(sn, (it + 1) & 1);
+        accumulate(vbuf(u), pf);
+        // one schedule for the whole step: S(t+1) MFMAs each followed by the
+        // next K read and a share of tile t's exponentiation, then the PV
+        // MFMAs each followed by the next two V^T reads
+        sched_step<NKB * NQC, 1, NDB * NKS, 2, 4, kExpValuPerTile / (NKB * NQC)>();
+      }
       if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];

@@ -99,6 +99,18 @@ __device__ __forceinline__ void dma16_buf(const void* base, uint32_t voffset, ui
                                            voffset, 0, 0, STREAM ? kNonTemporal : 0);
 }
 
+// The same with a uniform byte offset (soffset) added to every lane's: the
+// row part of a copy's source offset, kept on the scalar unit.
+template <bool STREAM>
+__device__ __forceinline__ void dma16_buf_s(const void* base, uint32_t voffset, uint32_t soffset,
+                                            uint16_t* lds_seg) {
+  constexpr int kNonTemporal = 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_seg, 16,
+                                           voffset, soffset, 0, STREAM ? kNonTemporal : 0);
+}
+
 // Scheduling hints (sched_group_barrier masks: 0x2 VALU, 0x8 MFMA, 0x100
 // DS read). One pipeline step: N1 MFMAs that each consume R1 LDS reads and
 // may hide V1 VALU instructions, then N2 MFMAs consuming R2 reads each. The
