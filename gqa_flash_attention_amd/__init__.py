@@ -14,8 +14,8 @@ import torch
 
 from ._lib import FAError, ScoreMods, check, load  # noqa: F401
 
-__all__ = ["prefill", "decode_paged", "decode_paged_fp8", "decode_workspace_bytes", "combine_lse",
-           "kv_append", "kv_append_fp8", "paged_gather", "FAError", "load"]
+__all__ = ["prefill", "decode_paged", "decode_paged_noalloc", "decode_paged_fp8", "decode_workspace_bytes",
+           "combine_lse", "kv_append", "kv_append_fp8", "paged_gather", "FAError", "load"]
 
 
 def _ptr(t):
@@ -187,6 +187,45 @@ def decode_paged(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 1
                                          B, Sq, Hq, Hkv, Dk, Dv, num_pages, page_size, max_pages, kv_chunk,
                                          int(bool(causal)), int(window), float(scale), mref,
                                          _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, lse
+
+
+def decode_paged_noalloc(q, kcache, vcache, block_table, seq_lens, *, page_size: int = 16,
+                         kv_chunk: int = 256, causal: bool = True, window: int = 0,
+                         scale: float | None = None, out=None, lse=None, softcap: float = 0.0,
+                         max_bias: float = 0.0, sinks=None, mask=None):
+    """decode_paged through fa_decode_paged_noalloc: the split partials go to
+    the library's static device buffer instead of a workspace, so the C call
+    allocates nothing (out and lse must then be given by a caller that cannot
+    allocate either). Calls on one GPU share the buffer: order them on one
+    stream. Raises FAError(FA_ERR_SCRATCH) when the call's partials exceed
+    the buffer (NOALLOC_SCRATCH_BYTES)."""
+    from ._lib import NOALLOC_SCRATCH_BYTES  # noqa: F401  (documented limit)
+
+    B, Sq, Hq, Dk = q.shape
+    dev = q.device
+    _require(q, "q", torch.bfloat16, dev, strided=True)
+    _require(kcache, "kcache", torch.bfloat16, dev, strided=True)
+    _require(vcache, "vcache", torch.bfloat16, dev, strided=True)
+    _lengths_table(seq_lens, block_table, B, dev)
+    Dv = vcache.shape[3]
+    if vcache.shape[:3] != kcache.shape[:3] or kcache.shape[3] != Dk:
+        raise ValueError("kcache / vcache shapes do not match q")
+    Hkv = kcache.shape[2]
+    num_pages, max_pages = _cache_geometry(kcache, vcache, block_table, page_size, dev, B, same_shape=False)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, Dv), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev, strided=True)
+    _shape(out, "out", (B, Sq, Hq, Dv))
+    lse = _lse_out(lse, B, Hq, Sq, dev)
+    mref, _keep = _mods(softcap, max_bias, sinks, mask, B, Sq, Hq, max_pages * page_size, dev)
+    check(load().fa_decode_paged_noalloc(_ptr(q), _strides(q), _ptr(kcache), _strides(kcache),
+                                         _ptr(vcache), _strides(vcache), _ptr(block_table),
+                                         _ptr(seq_lens), _ptr(out), _strides(out), _ptr(lse),
+                                         B, Sq, Hq, Hkv, Dk, Dv, num_pages, page_size, max_pages, kv_chunk,
+                                         int(bool(causal)), int(window), float(scale), mref, _stream(dev)))
     return out, lse
 
 

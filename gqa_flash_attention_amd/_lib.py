@@ -16,7 +16,9 @@ LIB_PATH = os.path.join(_HERE, "libgqafa.so")
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_INVALID_ARG", -2: "FA_ERR_UNSUPPORTED",
-                -3: "FA_ERR_WORKSPACE", -4: "FA_ERR_LAUNCH"}
+                -3: "FA_ERR_WORKSPACE", -4: "FA_ERR_LAUNCH", -5: "FA_ERR_SCRATCH"}
+# fa_decode_paged_noalloc's static device buffer (FA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol the C header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -38,6 +40,8 @@ SIGNATURES = {
     "fa_kv_append_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_paged_gather": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
 }

@@ -2,6 +2,7 @@
 // synchronizes, prints or aborts; an invalid call launches nothing.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/gqafa.h"
 #include "fa_launch.h"
@@ -102,6 +103,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported shape (head dims must be multiples of 8 up to 512; page size a power of two)";
     case FA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "the call needs more device scratch than fa_decode_paged_noalloc's static buffer holds "
+             "(FA_NOALLOC_SCRATCH_BYTES); use fa_decode_paged_strided with a caller workspace";
     default: return "unknown status";
   }
 }
@@ -376,3 +380,78 @@ int fa_paged_gather(const void* cache, const int32_t* block_table, const int32_t
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode / verify without allocation: the split partials go to a static
+// device array of FA_NOALLOC_SCRATCH_BYTES that each GPU holds for the life
+// of the process, instead of a caller workspace.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each device: the array's name is a host-side
+// stand-in, so the address is looked up once per device (with that device
+// current) and kept. Devices past the table are looked up on every call.
+constexpr int kScratchDevs = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevs] = {};
+
+int scratch_address(int dev, void** out) {
+  if (dev >= 0 && dev < kScratchDevs) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] != nullptr) {
+      *out = g_scratch_ptr[dev];
+      return FA_OK;
+    }
+  }
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+  if (e != hipSuccess || ptr == nullptr) return FA_ERR_LAUNCH;
+  if (dev >= 0 && dev < kScratchDevs) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = ptr;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_decode_paged_noalloc(const void* q, const int64_t* q_stride,
+                                       const void* kcache, const int64_t* k_stride,
+                                       const void* vcache, const int64_t* v_stride,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       void* o, const int64_t* o_stride, float* lse,
+                                       int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
+                                       int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                                       int causal, int window, float scale, const fa_score_mods* mods,
+                                       void* stream) {
+  // size check first: the partials of this call must fit the static array
+  if (B >= 0 && Sq >= 0 && Hq > 0 && max_pages_per_seq >= 0 && head_dim_ok(Dk) && head_dim_ok(Dv)) {
+    const int ps = log2_exact(page_size);
+    const int64_t max_len = ps >= 0 ? ((int64_t)max_pages_per_seq << ps) : 0;
+    if (ps >= 0 && ps <= 16 && max_len <= INT32_MAX && kv_chunk > 0 && kv_chunk % 32 == 0) {
+      const size_t need = fa_decode_workspace_bytes(B, Sq, Hq, Dk > Dv ? Dk : Dv, (int)max_len, kv_chunk);
+      if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    }
+  }
+  // the array of the stream's device (a stream belongs to one device)
+  int dev = 0;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess) return FA_ERR_INVALID_ARG;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return FA_ERR_LAUNCH;
+  }
+  void* ws = nullptr;
+  const int st = scratch_address(dev, &ws);
+  if (st != FA_OK) return st;
+  return decode_impl(q, q_stride, kcache, k_stride, vcache, v_stride, nullptr, nullptr, false, block_table,
+                     seq_lens, o, o_stride, lse, B, Sq, Hq, Hkv, Dk, Dv, num_pages, page_size,
+                     max_pages_per_seq, kv_chunk, causal, window, scale, mods, ws,
+                     (size_t)FA_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -51,7 +51,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad mask or scale, misaligned pointer */
   FA_ERR_UNSUPPORTED = -2,  /* head dim not a multiple of 8 in [8, 512], page size not a power of two */
   FA_ERR_WORKSPACE = -3,    /* decode workspace missing or smaller than fa_decode_workspace_bytes */
-  FA_ERR_LAUNCH = -4        /* the HIP runtime rejected a kernel launch */
+  FA_ERR_LAUNCH = -4,       /* the HIP runtime rejected a kernel launch */
+  FA_ERR_SCRATCH = -5       /* fa_decode_paged_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /*
@@ -325,6 +326,39 @@ int fa_kv_append_fp8(void* kcache, const int64_t* k_stride, void* vcache, const 
                      const void* knew, const int64_t* knew_stride, const void* vnew, const int64_t* vnew_stride,
                      int B, int Snew, int Hkv, int D, int num_pages, int page_size, int max_pages_per_seq,
                      void* stream);
+
+/*
+ * fa_decode_paged_strided for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with the split partials written to a static
+ * device array of FA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends, instead of a caller workspace.
+ * Every argument is as fa_decode_paged_strided without the workspace; the
+ * results are bitwise those of fa_decode_paged_strided.
+ *
+ *   - A call whose fa_decode_workspace_bytes(B, Sq, Hq, max(Dk, Dv),
+ *     max_pages_per_seq * page_size, kv_chunk) exceeds
+ *     FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_SCRATCH and launches nothing.
+ *   - Nothing here allocates: the array's address on a device is looked up
+ *     (hipGetSymbolAddress) on the first call for that device and kept.
+ *   - The array is shared by every call on its GPU and keeps the last call's
+ *     partials; a call writes every slot it reads before reading it, so
+ *     nothing needs clearing. Calls that overlap on one GPU (on different
+ *     streams, or from different threads, without ordering) race on the
+ *     array: order them on one stream.
+ *   - The array used is that of the stream's device (the current device for
+ *     the NULL stream).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fa_decode_paged_noalloc(const void* q, const int64_t* q_stride,
+                            const void* kcache, const int64_t* k_stride,
+                            const void* vcache, const int64_t* v_stride,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            void* o, const int64_t* o_stride, float* lse,
+                            int B, int Sq, int Hq, int Hkv, int Dk, int Dv,
+                            int num_pages, int page_size, int max_pages_per_seq, int kv_chunk,
+                            int causal, int window, float scale, const fa_score_mods* mods,
+                            void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["fa_prefill", "fa_prefill_strided", "fa_decode_workspace_bytes",
                             "fa_decode_paged", "fa_decode_paged_strided", "fa_combine_lse",
                             "fa_kv_append", "fa_status_string", "fa_paged_gather",
-                            "fa_decode_paged_fp8", "fa_kv_append_fp8"])
+                            "fa_decode_paged_fp8", "fa_kv_append_fp8", "fa_decode_paged_noalloc"])
     assert set(names) == set(_lib.SIGNATURES)
 
 
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 12345):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, -5, 12345):
         assert lib.fa_status_string(s)
 
 
