@@ -394,12 +394,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const int rsb = ES * rs;                          // bytes per key row
       const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
       const uint32_t lro = is_v ? p_lrv : p_lrk;        // p_lr * rsb
-#pragma unroll
-      for (int i = 0; i < SEGW; ++i) {
+      auto seg_copy = [&](int i, bool clamp_rows) {
         const int sg = wave * SEGW + i;                 // uniform
         const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
         uint32_t o = lro + 16u * (uint32_t)lc;
-        if (tail) {
+        if (clamp_rows) {
           // rows past the last valid one read that row instead (their scores
           // are masked, their V rows get weight 0)
           const int r = sg * RPS + p_lr;
@@ -410,6 +409,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           if (8 * lc >= (is_v ? a.dv : a.dk)) o -= 16u * (uint32_t)lc;
         }
         dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
+      };
+      // At head dim 512 whole tiles (all but a sequence's last) take a
+      // straight-line path (the per-copy tail test became a branch per copy
+      // there); elsewhere one loop keeps the register budget.
+      if (D < 512 || tail) {
+#pragma unroll
+        for (int i = 0; i < SEGW; ++i) seg_copy(i, tail);
+      } else {
+#pragma unroll
+        for (int i = 0; i < SEGW; ++i) seg_copy(i, false);
       }
       return;
     }
@@ -1298,11 +1307,26 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const int tb = t_start + it * BN;
       if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
       lds_barrier();
+      // At head dim 512 (one wave per SIMD) the partner's scores are read
+      // first, so their LDS latency overlaps the copy issue below (measured:
+      // 1.79 -> 1.63 ms for the head-dim-512 causal workload; at head dim 256,
+      // two waves per SIMD, the other order is 2 % faster); they are added
+      // in once the first MFMAs of S(t+1) are under way.
+      constexpr bool kBig = D >= 512;
+      float oth[kBig ? 16 : 1];
+      if constexpr (kBig) {
+        static_assert(DS == 2 && NKB == 1, "head dim 512: two waves share the scores of a 32-key tile");
+#pragma unroll
+        for (int x = 0; x < 16; ++x) oth[x] = sX[it & 1][wave ^ 1][x][lane];
+      }
       load_mask(tb);
       if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
       if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
-      combine_partner(sc, it & 1);
-      const float nb = prepare(sc, tb);
+      float nb = 0.f;
+      if constexpr (!kBig) {
+        combine_partner(sc, it & 1);
+        nb = prepare(sc, tb);
+      }
       f32x16 sn[NKB];
       // Up to D = 128 two workgroups share a CU, so each SIMD runs waves of
       // both. A wave raises its priority for its MFMA block and drops it for
@@ -1316,8 +1340,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // to keep more than one operand read in flight on its own. The step
         // is written in explicit batches instead: the reads of the next
         // batch are issued before the MFMAs of the current one (a schedule
-        // fence between batches), and tile t's exponentiation is spread
-        // over the S(t+1) batches.
+        // fence between batches); the first batch of S(t+1) is issued before
+        // tile t's exchange and softmax bookkeeping, which then run while it
+        // computes, and tile t's exponentiation is spread over the other
+        // S(t+1) batches.
         const uint16_t* bk = kbuf((u + 1) % NBUF);
         const uint16_t* bv = vbuf(u);
         constexpr int KB = 4;                    // MFMAs per batch
@@ -1328,6 +1354,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           const int ch = 2 * (c + dh * NQC) + hl;
           return *reinterpret_cast<const u32x4*>(&bk[j * D + 8 * (ch ^ swz_k<D>(j))]);
         };
+        static_assert(NSB >= 2, "the exponentiation needs a batch after the first");
         u32x4 kf[2][KB];
 #pragma unroll
         for (int x = 0; x < KB; ++x) kf[0][x] = kread(x);
@@ -1343,10 +1370,21 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           }
 #pragma unroll
           for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
-          // pairs q with q * NSB / NPAIR == bi: an even share per batch
+          if (bi == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            // the partner's half of tile t's scores (same order in both
+            // waves, so the pair holds bit-identical sums), then the mask and
+            // the running max
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sc[0][x] = dh == 0 ? sc[0][x] + oth[x] : oth[x] + sc[0][x];
+            nb = prepare(sc, tb);
+            continue;
+          }
+          // pairs q with q (NSB - 1) / NPAIR == bi - 1: an even share per
+          // batch after the first
 #pragma unroll
           for (int q = 0; q < NPAIR; ++q) {
-            if (q * NSB / NPAIR != bi) continue;
+            if (q * (NSB - 1) / NPAIR != bi - 1) continue;
             const int ks = q / 4, w = q % 4, base = 8 * (ks & 1);
             const float e0 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w], sl2, nb));
             const float e1 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w + 1], sl2, nb));

@@ -8,6 +8,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 
 #include "fa_attn_kernel.h"
 #include "fa_launch.h"
@@ -47,21 +48,31 @@ template <int D, int NWR> struct SplitCfg {
 // Workgroups of a kernel the GPU holds at once: CUs x resident workgroups per
 // CU. Measured on MI355X, a CU holds at most 144 KiB of LDS across
 // workgroups of 32 KiB or less (the occupancy query allows 160), so the
-// count is the smaller of the two.
+// count is the smaller of the two. The device is the stream's (the current
+// one for the null stream). The answer is kept per device (the library's
+// only process state besides the no-allocation scratch array: a pure
+// function of the kernel and the device); devices past the table are
+// queried on every call.
+constexpr int kResidentDevs = 64;
 template <typename Kernel>
-int resident_workgroups(Kernel kernel, int threads, int* cache) {
+int resident_workgroups(Kernel kernel, int threads, std::atomic<int>* cache, hipStream_t stream) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (cache[dev] > 0) return cache[dev];
+  const bool known = (stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) == hipSuccess;
+  const bool keep = known && dev >= 0 && dev < kResidentDevs;
+  if (keep) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int occ = 0, cus = 0;
   hipFuncAttributes attr{};
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess) occ = 1;
   if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) == hipSuccess &&
       attr.sharedSizeBytes > 0)
     occ = std::min<int>(occ, (int)(147456 / attr.sharedSizeBytes));
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
-  cache[dev] = std::max(occ, 1) * std::max(cus, 1);
-  return cache[dev];
+  if (!known || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+  const int n = std::max(occ, 1) * std::max(cus, 1);
+  if (keep) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int D, int NWR>
@@ -115,9 +126,9 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
        attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE_MASK, 4>}};
   const int paged = d.table != nullptr ? 1 : 0;
   K k = kernels[paged][level];
-  int* cache_row;
+  std::atomic<int>* cache_row;
   // the grid is what the chosen kernel holds resident
-  static int cache[2][5][16];
+  static std::atomic<int> cache[2][5][kResidentDevs];
   cache_row = cache[paged][level];
   if constexpr (D == 128) {
     if (d.kv8) {
@@ -128,13 +139,13 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
            attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE_MASK, 2, true>},
           {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE8, 0, true>,
            attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE_MASK, 2, true>}};
-      static int cache8[2][2][16];
+      static std::atomic<int> cache8[2][2][kResidentDevs];
       const int l8 = level == 0 ? 0 : 1;
       k = kernels8[paged][l8];
       cache_row = cache8[paged][l8];
     }
   }
-  const int resident = resident_workgroups(k, NW * 64, cache_row);
+  const int resident = resident_workgroups(k, NW * 64, cache_row, stream);
   // whole sets of Hkv workgroups, one per KV head
   const int grid = std::max(resident / d.Hkv, 1) * d.Hkv;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
