@@ -357,6 +357,45 @@ def bench_fp8(torch, fa, workloads, dev, steps, warmup):
                            "speedup_vs_bf16": round(ref["ms_per_call_median"] / ms, 3)}
         del kc, vc, q, ws, o, lse, table, lens
         torch.cuda.empty_cache()
+    # head dims 256 and 512 (the head sizes of the large-head layers): decode
+    # with the decode workload's lengths, B=16, Hq=16, Hkv=8, contiguous
+    # caches, 256-token chunks; bf16 beside
+    import dataclasses
+    for D in (256, 512):
+        shape = dataclasses.replace(workloads.C3, name=f"decode_d{D}", Hq=16, D=D)
+        print(f"{shape.name} bf16", file=sys.stderr, flush=True)
+        ref = bench_decode(torch, fa, workloads, dev, shape, steps, warmup, flush)
+        torch.cuda.empty_cache()
+        print(f"{shape.name} fp8", file=sys.stderr, flush=True)
+        di = workloads.decode_inputs(shape)
+        g = torch.Generator("cpu").manual_seed(809 + D)
+        kc = torch.randint(0, 0x7F, di.kcache.shape, generator=g, dtype=torch.int32).to(torch.uint8).to(dev)
+        vc = torch.randint(0, 0x7F, di.vcache.shape, generator=g, dtype=torch.int32).to(torch.uint8).to(dev)
+        ks = torch.full((shape.Hkv,), 4.0 / 448, dtype=torch.float32, device=dev)
+        q, lens = di.q.to(dev), di.seq_lens.to(dev)
+        ws = torch.empty(fa.decode_workspace_bytes(shape.B, shape.Sq, shape.Hq, D, shape.max_len, shape.kv_chunk),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((shape.B, shape.Hq, shape.Sq), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.decode_paged_fp8(q, kc, vc, ks, ks, None, lens, page_size=16, kv_chunk=shape.kv_chunk, causal=True,
+                                scale=shape.scale, workspace=ws, out=o, lse=lse)
+
+        for _ in range(warmup):
+            step()
+        per, _, _ = time_calls(torch, step, steps, flush=flush)
+        ms = sorted(per)[len(per) // 2]
+        bf16_bytes = decode_bytes(shape, di.seq_lens.tolist())
+        kv_bf16 = sum(int(n) for n in di.seq_lens.tolist()) * shape.Hkv * shape.D * 2 * 2
+        nbytes = bf16_bytes - kv_bf16 // 2
+        out[shape.name] = {"fp8_ms_per_call_median": round(ms, 4), "fp8_algorithmic_bytes": nbytes,
+                           "fp8_GB_s": round(nbytes / ms / 1e6, 1),
+                           "fp8_frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                           "bf16_ms_per_call_median": ref["ms_per_call_median"], "bf16_GB_s": ref["GB_s"],
+                           "speedup_vs_bf16": round(ref["ms_per_call_median"] / ms, 3)}
+        del kc, vc, q, ws, o, lse, lens, di
+        torch.cuda.empty_cache()
     return out
 
 

@@ -256,11 +256,11 @@ def decode_paged_fp8(q, kcache, vcache, k_scale, v_scale, block_table, seq_lens,
                      sinks=None, mask=None):
     """Split-KV decode / verify over fp8 (OCP e4m3) caches.
 
-    kcache / vcache: uint8 [num_pages, page_size, Hkv, 128] with block_table,
-    else [B, Smax, Hkv, 128] (views with a unit-stride last dimension);
-    k_scale / v_scale: fp32 [Hkv] dequantisation scales (value = e4m3(byte) *
-    scale). q and the result are bf16 [B, Sq, Hq, 128]; the rest is as
-    decode_paged.
+    kcache / vcache: uint8 [num_pages, page_size, Hkv, D] with block_table,
+    else [B, Smax, Hkv, D], D = 128, 256 or 512 (views with a unit-stride
+    last dimension); k_scale / v_scale: fp32 [Hkv] dequantisation scales
+    (value = e4m3(byte) * scale). q and the result are bf16 [B, Sq, Hq, D];
+    the rest is as decode_paged.
     """
     B, Sq, Hq, D = q.shape
     dev = q.device

@@ -163,7 +163,8 @@ size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, 
 namespace {
 
 // Decode / verify behind fa_decode_paged_strided (bf16 caches) and
-// fa_decode_paged_fp8 (one-byte e4m3 caches with per-head scales, D = 128).
+// fa_decode_paged_fp8 (one-byte e4m3 caches with per-head scales, D = 128,
+// 256 or 512).
 int decode_impl(const void* q, const int64_t* q_stride,
                 const void* kcache, const int64_t* k_stride,
                 const void* vcache, const int64_t* v_stride,
@@ -175,7 +176,7 @@ int decode_impl(const void* q, const int64_t* q_stride,
                 int causal, int window, float scale, const fa_score_mods* mods,
                 void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-  if (kv8 && (Dk != 128 || Dv != 128)) return FA_ERR_UNSUPPORTED;
+  if (kv8 && (Dk != Dv || (Dk != 128 && Dk != 256 && Dk != 512))) return FA_ERR_UNSUPPORTED;
   Mods md;
   if (!get_mods(mods, md)) return FA_ERR_INVALID_ARG;
   // chunks are whole 32-key tiles

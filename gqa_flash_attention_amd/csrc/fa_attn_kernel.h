@@ -63,7 +63,7 @@
 // slope); 2 the transform plus an additive bf16 mask; 3 and 4 are 0 and 2 on
 // head dims below the tile width D (Q columns past Dk load as 0, K/V chunks
 // past Dk / Dv are filled from chunk 0 of the same key row, O columns past
-// Dv are not stored). KV8 (split kernels at D = 128) reads one-byte OCP e4m3
+// Dv are not stored). KV8 (split kernels at D = 128, 256, 512) reads one-byte OCP e4m3
 // K/V tiles and widens each fragment to bf16 just before its MFMA; the K/V
 // scales of the workgroup's KV head fold into the exponent factor and the
 // partial's normalisation.
@@ -243,7 +243,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   constexpr bool kPad = MODS >= 3;
   // fp8 K/V (one byte per element) only in the one-wave-per-32-rows split
   // kernels at D = 128 (8 chunks of 16 bytes per key row)
-  static_assert(!KV8 || (SPLIT && DS == 1 && D == 128 && !kPad), "fp8 K/V: D = 128 split kernels");
+  // fp8 K/V (one byte per element): split kernels at head dims 128, 256 and
+  // 512 (register-staged one wave per 32 rows at 128, a D split above)
+  static_assert(!KV8 || (SPLIT && D >= 128 && !kPad && (D == 128) == (DS == 1)), "fp8 K/V: split kernels");
   constexpr int ES = KV8 ? 1 : 2;             // bytes per K/V element
   constexpr int KCH = D * ES / 16;            // 16-byte chunks per row
   constexpr int NSEG = BN * KCH / 64;         // 1 KiB segments per tile
@@ -600,9 +602,18 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {          // alternate accumulators
         const int row = 32 * kb + j;
-        const int ch = 2 * (c + dh * NQC) + hl;
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
-        s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
+        if constexpr (KV8) {
+          // fp8 tile: this lane's 8 bytes (d = 16 c' + 8 hl ..) of its key
+          // row in 16-byte chunk c' = c + dh NQC, widened to bf16
+          const unsigned char* b8 = reinterpret_cast<const unsigned char*>(bk);
+          const u32x2 kw =
+              *reinterpret_cast<const u32x2*>(b8 + row * D + 16 * ((c + dh * NQC) ^ swzk(row)) + 8 * hl);
+          s[kb] = mfma32(as_bf16x8(fp8x8_to_bf16x8(kw)), qf[c], s[kb]);
+        } else {
+          const int ch = 2 * (c + dh * NQC) + hl;
+          const u32x4 kw = *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
+          s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
+        }
       }
     }
   };
@@ -720,6 +731,23 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 
   // O^T += V^T P^T for the tile in bv
   auto accumulate = [&](const uint16_t* bv, const u32x4 (&pf)[NKS]) {
+    if constexpr (KV8) {
+      // fp8 tile: V^T from ds_read_b64_tr_b8 (lane layout as read_v8 below,
+      // the d block offset by this wave's part of the head dim), widened to
+      // bf16 just before the MFMA
+      const unsigned char* b8 = reinterpret_cast<const unsigned char*>(bv);
+      const int grp = lane >> 4, r16 = lane & 15, aa = r16 & 1, kk = r16 >> 1;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int row = 16 * ks + 8 * (kk >> 2) + 4 * (grp >> 1) + (kk & 3);
+          const int lc = 2 * (db + dh * NDB) + (grp & 1);
+          const u32x2 vw = read_tr8(b8 + row * D + 16 * (lc ^ swzv(row)) + 8 * aa);
+          oacc[db] = mfma32(as_bf16x8(fp8x8_to_bf16x8(vw)), as_bf16x8(pf[ks]), oacc[db]);
+        }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll

@@ -40,9 +40,13 @@ template <int D, int NWR> struct SplitCfg {
   // Wider workgroups are held by registers at two waves per SIMD and take
   // deeper rings instead (three for the paged two-wave kernel, which holds
   // no more within its register budget).
-  static constexpr int NBUF8 = NW == 1 ? 2 : 4;
-  static constexpr int NBUF8P = NW == 1 ? 2 : (NW == 2 ? 3 : 4);
+  static constexpr int NBUF8 = (NW == 1 || D > 128) ? 2 : 4;
+  static constexpr int NBUF8P = (NW == 1 || D > 128) ? 2 : (NW == 2 ? 3 : 4);
+  // Above head dim 128 the fp8 kernels split D over the waves of 32 rows as
+  // the bf16 ones do, with the half-size tiles in a two-buffer ring (two
+  // workgroups per CU at 256, one at 512 by LDS).
   static constexpr int WPE8 = 2;
+  static constexpr int WPE8_MASK = D == 128 ? WPE_MASK : 2;
 };
 
 // Workgroups of a kernel the GPU holds at once: CUs x resident workgroups per
@@ -130,15 +134,15 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   // the grid is what the chosen kernel holds resident
   static std::atomic<int> cache[2][5][kResidentDevs];
   cache_row = cache[paged][level];
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     if (d.kv8) {
       // fp8 caches: plain, or score transform and mask (softcap / ALiBi alone
       // run with a null mask)
       static const K kernels8[2][2] = {
           {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE8, 0, true>,
-           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE_MASK, 2, true>},
+           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE8_MASK, 2, true>},
           {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE8, 0, true>,
-           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE_MASK, 2, true>}};
+           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE8_MASK, 2, true>}};
       static std::atomic<int> cache8[2][2][kResidentDevs];
       const int l8 = level == 0 ? 0 : 1;
       k = kernels8[paged][l8];

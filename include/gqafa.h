@@ -237,7 +237,10 @@ int fa_decode_paged_strided(const void* q, const int64_t* q_stride,
  *                   for the contiguous layout; multiples of 16 below 2^40,
  *                   token strides below 2^24
  *   k_scale, v_scale    device fp32 [Hkv], 4-byte aligned
- *   D               128 (FA_ERR_UNSUPPORTED otherwise)
+ *   D               128, 256 or 512 (FA_ERR_UNSUPPORTED otherwise): the head
+ *                   sizes of the pages' quantised-cache layers (llama.cpp
+ *                   PR 28507, Measurements: q8_0 caches on head-256 SWA and
+ *                   head-512 global layers)
  * Everything else (q and o bf16, seq_lens, block table, workspace, score
  * modifiers, outputs) is as fa_decode_paged_strided with Dk = Dv = D. The
  * arithmetic is that of the bf16 cache path on the dequantised values: the

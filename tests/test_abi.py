@@ -229,7 +229,8 @@ def test_fp8_decode_validation(lib):
         return f(P, None, P, ks, P, None, ksc, vsc, P, P, P, None, None, B, 1, 8, 2, D, 64, 16, 8, 64, 1, 0,
                  0.1, None, P, 1 << 30, None)
     assert call() == OK
-    assert call(D=64) == UNSUPPORTED and call(D=256) == UNSUPPORTED
+    assert call(D=256) == OK and call(D=512) == OK
+    assert call(D=64) == UNSUPPORTED and call(D=192) == UNSUPPORTED and call(D=320) == UNSUPPORTED
     assert call(ks=_st(0, 2 * 2 * 128, 128)) == OK           # K/V interleaved per slot, 16-byte rows
     assert call(ks=_st(0, 8 * 2, 8)) == INVALID              # not a multiple of 16 bytes
     assert call(B=2, ksc=None) == INVALID and call(B=2, vsc=P + 2) == INVALID

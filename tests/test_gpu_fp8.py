@@ -80,9 +80,9 @@ DECODE = [
 ]
 
 
-def _fp8_case(case, seed):
+def _fp8_case(case, seed, D=128):
     B, Sq, Hq, Hkv, ps, max_len, (lo, hi), chunk = case
-    shape = workloads.DecodeShape("fp8", B=B, Sq=Sq, Hq=Hq, Hkv=Hkv, D=128, page_size=ps, max_len=max_len,
+    shape = workloads.DecodeShape("fp8", B=B, Sq=Sq, Hq=Hq, Hkv=Hkv, D=D, page_size=ps, max_len=max_len,
                                   len_lo=lo, len_hi=hi, kv_chunk=chunk, seed=seed)
     di = workloads.decode_inputs(shape)
     g = torch.Generator().manual_seed(seed + 1)
@@ -219,3 +219,71 @@ def test_fp8_decode_window():
     o_ref, lse_ref = oracle.decode_paged_ref(di.q, _deq(kc, ks), _deq(vc, vs), di.block_table, di.seq_lens,
                                              page_size=16, causal=True, window=100, scale=shape.scale)
     assert_parity(o, lse, o_ref, lse_ref, "fp8 verify window 100")
+
+
+# head dims 256 and 512 (the pages' quantised-cache layers: head 256 on SWA
+# layers, 512 on global layers): the D-split fp8 kernels
+LARGE = [
+    # D, B, Sq, Hq, Hkv, page_size (0 = contiguous), max_len, len range, chunk
+    (256, 3, 1, 16, 8, 16, 1024, (1, 1024), 128),
+    (256, 2, 8, 32, 4, 0, 768, (8, 768), 256),          # 64 rows per KV head: two row groups
+    (256, 2, 2, 8, 1, 64, 256, (0, 256), 64),            # zero-length sequences possible
+    (512, 3, 1, 16, 8, 16, 1024, (1, 1024), 128),
+    (512, 2, 4, 32, 4, 0, 512, (4, 512), 96),            # 32 rows per KV head, several row blocks
+    (512, 20, 2, 8, 4, 16, 2048, (1, 2048), 32),         # several ranges per workgroup set
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=lambda c: "D{}_B{}_Sq{}_H{}x{}_ps{}_L{}_{}_c{}".format(*c))
+def test_fp8_decode_large_head_dims(case):
+    print(f"fp8 decode large head dim {case}", flush=True)
+    D = case[0]
+    shape, di, kc, vc, ks, vs = _fp8_case(case[1:], seed=case[1] * 17 + D + case[2], D=D)
+    ps = shape.page_size or 16
+    table = None if di.block_table is None else di.block_table.to(DEV)
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV), table,
+                                 di.seq_lens.to(DEV), page_size=ps, kv_chunk=shape.kv_chunk, causal=True,
+                                 scale=shape.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, _deq(kc, ks), _deq(vc, vs), di.block_table, di.seq_lens,
+                                             page_size=ps, causal=True, scale=shape.scale)
+    assert_parity(o, lse, o_ref, lse_ref, f"fp8 decode D{D} {case}")
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_fp8_large_head_dims_modifiers_and_append(D):
+    """Every score modifier and a window over an fp8 cache at head dim 256 /
+    512, then an fp8 append of 4 new rows and the verify over the result."""
+    case = (2, 4, 16, 2, 16, 640, (300, 640), 128)
+    shape, di, kc, vc, ks, vs = _fp8_case(case, seed=1200 + D, D=D)
+    g = torch.Generator().manual_seed(1300 + D)
+    sinks = torch.randn(shape.Hq, generator=g).float()
+    mask = (2.0 * torch.randn(shape.B, shape.Sq, shape.max_len, generator=g)).to(torch.bfloat16)
+    mask[:, :, 5:11] = -float("inf")
+    kw = dict(softcap=20.0, max_bias=4.0)
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV),
+                                 di.block_table.to(DEV), di.seq_lens.to(DEV), page_size=16, kv_chunk=128,
+                                 causal=True, window=200, scale=shape.scale, sinks=sinks.to(DEV),
+                                 mask=mask.to(DEV), **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, _deq(kc, ks), _deq(vc, vs), di.block_table, di.seq_lens,
+                                             page_size=16, causal=True, window=200, scale=shape.scale,
+                                             sinks=sinks.double().numpy(), mask=mask, **kw)
+    assert_parity(o, lse, o_ref, lse_ref, f"fp8 D{D} all modifiers")
+    # append 4 new rows (placed at the end of each sequence), then verify
+    Hkv = shape.Hkv
+    kn = torch.randn(shape.B, 4, Hkv, D, generator=g).to(torch.bfloat16)
+    vn = torch.randn(shape.B, 4, Hkv, D, generator=g).to(torch.bfloat16)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    fa.kv_append_fp8(kd, vd, ks.to(DEV), vs.to(DEV), di.block_table.to(DEV), di.seq_lens.to(DEV), kn.to(DEV),
+                     vn.to(DEV), page_size=16)
+    o, lse = fa.decode_paged_fp8(di.q.to(DEV), kd, vd, ks.to(DEV), vs.to(DEV), di.block_table.to(DEV),
+                                 di.seq_lens.to(DEV), page_size=16, kv_chunk=128, causal=True, scale=shape.scale)
+    torch.cuda.synchronize()
+    k2, v2 = oracle.kv_append_fp8_ref(kc.numpy(), vc.numpy(), di.block_table.numpy(), di.seq_lens.numpy(), kn,
+                                      vn, ks.numpy(), vs.numpy(), page_size=16)
+    assert np.array_equal(kd.cpu().numpy(), k2) and np.array_equal(vd.cpu().numpy(), v2)
+    o_ref, lse_ref = oracle.decode_paged_ref(di.q, oracle.dequantize_e4m3(k2, ks.numpy()),
+                                             oracle.dequantize_e4m3(v2, vs.numpy()), di.block_table, di.seq_lens,
+                                             page_size=16, causal=True, scale=shape.scale)
+    assert_parity(o, lse, o_ref, lse_ref, f"fp8 D{D} append + verify")
