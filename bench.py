@@ -399,7 +399,8 @@ def bench_fp8(torch, fa, workloads, dev, steps, warmup):
     return out
 
 
-HEAD_DIMS = [(80, 80), (96, 96), (128, 128), (192, 128), (192, 192), (256, 256), (320, 256), (512, 512)]
+HEAD_DIMS = [(80, 80), (96, 96), (128, 128), (192, 128), (192, 192), (256, 256), (320, 256), (512, 512),
+             (576, 512)]
 
 
 def bench_head_dims(torch, fa, workloads, dev, steps, warmup):

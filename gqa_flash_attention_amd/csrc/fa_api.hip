@@ -20,8 +20,16 @@ bool tile_dim_ok(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 // Head dims: multiples of 8 (16-byte rows) from 8 to 512.
 bool head_dim_ok(int D) { return D >= 8 && D <= 512 && D % 8 == 0; }
 
+// Key head dim 576 with value head dim 512: the 512 tile plus 64 extra key
+// columns (the 576/512 pair of the llama.cpp PR 28507 report's case grid).
+constexpr int kWideK = 576;
+bool wide_pair(int dk, int dv) { return dk == kWideK && dv == 512; }
+
+// (Dk, Dv) pairs the attention kernels run.
+bool dims_ok(int dk, int dv) { return (head_dim_ok(dk) && head_dim_ok(dv)) || wide_pair(dk, dv); }
+
 // The tile width that runs key / value head dims dk and dv: the smallest of
-// 64, 128, 256, 512 that holds both.
+// 64, 128, 256, 512 that holds both (512 for the 576-wide keys).
 int tile_dim(int dk, int dv) {
   const int m = dk > dv ? dk : dv;
   return m <= 64 ? 64 : (m <= 128 ? 128 : (m <= 256 ? 256 : 512));
@@ -100,7 +108,9 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
-    case FA_ERR_UNSUPPORTED: return "unsupported shape (head dims must be multiples of 8 up to 512; page size a power of two)";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported shape (head dims must be multiples of 8 up to 512, or 576 keys with 512 values; "
+             "page size a power of two)";
     case FA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_SCRATCH:
@@ -120,7 +130,7 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return FA_ERR_UNSUPPORTED;
+  if (!dims_ok(Dk, Dv)) return FA_ERR_UNSUPPORTED;
   Strides qs, ks, vs, os;
   const Strides qd{(int64_t)Sq * Hq * Dk, (int64_t)Hq * Dk, Dk};
   const Strides od{(int64_t)Sq * Hq * Dv, (int64_t)Hq * Dv, Dv};
@@ -148,7 +158,8 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 size_t fa_decode_workspace_bytes(int B, int Sq, int Hq, int D, int max_seq_len, int kv_chunk) {
-  if (B < 0 || Sq < 0 || Hq <= 0 || !head_dim_ok(D) || max_seq_len < 0 || kv_chunk <= 0 || kv_chunk % 32 != 0)
+  if (B < 0 || Sq < 0 || Hq <= 0 || !(head_dim_ok(D) || D == kWideK) || max_seq_len < 0 || kv_chunk <= 0 ||
+      kv_chunk % 32 != 0)
     return 0;
   const int64_t slots = n_chunks_for(max_seq_len, kv_chunk) + 1;
   const int64_t rows = (int64_t)B * Hq * Sq;
@@ -184,7 +195,7 @@ int decode_impl(const void* q, const int64_t* q_stride,
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return FA_ERR_UNSUPPORTED;
+  if (!dims_ok(Dk, Dv)) return FA_ERR_UNSUPPORTED;
   const int D = tile_dim(Dk, Dv);
   const int page_shift = log2_exact(page_size);
   if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
@@ -311,7 +322,7 @@ int fa_kv_append(void* kcache, const int64_t* k_stride, void* vcache, const int6
                  int B, int Snew, int Hkv, int Dk, int Dv, int num_pages, int page_size,
                  int max_pages_per_seq, void* stream) {
   if (B < 0 || Snew < 0 || Hkv <= 0 || max_pages_per_seq < 0) return FA_ERR_INVALID_ARG;
-  if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return FA_ERR_UNSUPPORTED;
+  if (!dims_ok(Dk, Dv)) return FA_ERR_UNSUPPORTED;
   const int page_shift = log2_exact(page_size);
   if (page_shift < 0 || page_shift > 16) return FA_ERR_UNSUPPORTED;
   const int64_t max_len = (int64_t)max_pages_per_seq << page_shift;
@@ -433,7 +444,7 @@ extern "C" int fa_decode_paged_noalloc(const void* q, const int64_t* q_stride,
                                        int causal, int window, float scale, const fa_score_mods* mods,
                                        void* stream) {
   // size check first: the partials of this call must fit the static array
-  if (B >= 0 && Sq >= 0 && Hq > 0 && max_pages_per_seq >= 0 && head_dim_ok(Dk) && head_dim_ok(Dv)) {
+  if (B >= 0 && Sq >= 0 && Hq > 0 && max_pages_per_seq >= 0 && dims_ok(Dk, Dv)) {
     const int ps = log2_exact(page_size);
     const int64_t max_len = ps >= 0 ? ((int64_t)max_pages_per_seq << ps) : 0;
     if (ps >= 0 && ps <= 16 && max_len <= INT32_MAX && kv_chunk > 0 && kv_chunk % 32 == 0) {

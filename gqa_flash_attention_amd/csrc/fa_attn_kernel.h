@@ -229,7 +229,8 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
   return x;
 }
 
-template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, int MODS, bool KV8 = false>
+template <int D, int NW, int BN, int DS, int NBUF, bool PAGED, bool SPLIT, int WPE, int MODS, bool KV8 = false,
+          bool KX = false>
 __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
@@ -261,6 +262,17 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // contiguous-cache kernel reserves the same space, so both kernels hold
   // the same number of workgroups per CU and split the work identically.
   constexpr int TAB = (SPLIT && D < 512) ? 512 : 0;
+  // KX: a key head dim of D + 64 (576 at D = 512; the value head dim is D).
+  // The 64 extra key columns have a small tile of their own (32 rows x 64,
+  // one 1 KiB copy segment per wave), and each wave of a D split takes 64 / DS
+  // of them as NQX more 16-wide steps of the score contraction. The score
+  // exchange then has one slot (LDS: 128 KiB of tiles + 8 KiB of extra key
+  // columns + 16 KiB of exchange).
+  static_assert(!KX || (D == 512 && !KV8 && !kPad && (MODS == 0 || MODS == 2) && NW == 4 && NBUF == 2 && BN == 32),
+                "576-wide keys: the head-dim-512 kernels");
+  constexpr int DXK = KX ? 64 : 0;
+  constexpr int NQX = KX ? 4 / DS : 1;
+  constexpr int XSLOTS = KX ? 1 : 2;
 
   // A ring of NBUF tile buffers per operand, each its own object: the copies
   // into one never alias reads of another, so no read waits on a copy it does
@@ -282,7 +294,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     asm volatile("" ::"v"(sT_buf));           // keeps the reservation in the dense kernel
   }
   // partial scores exchanged by the waves of a D split, [slot][wave][value][lane]
-  __shared__ float sX[DS > 1 ? 2 : 1][DS > 1 ? NW : 1][DS > 1 ? NKB * 16 : 1][64];
+  __shared__ float sX[DS > 1 ? XSLOTS : 1][DS > 1 ? NW : 1][DS > 1 ? NKB * 16 : 1][64];
+  // extra key columns (KX), one buffer per K tile buffer
+  __shared__ __attribute__((aligned(1024))) uint16_t sKx0[KX ? BN * DXK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sKx1[KX ? BN * DXK : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -385,6 +400,30 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     const int lim = ke_t - 1 - tb;            // last valid row of this tile
     const bool tail = lim < BN - 1;           // uniform
     const int rs = is_v ? v_rs : k_rs;
+    if constexpr (KX) {
+      if (!is_v) {
+        // the 64 extra key columns of the tile: wave w copies rows 8 w ..
+        // 8 w + 7 (8 chunks of 16 bytes each), logical chunk (lane & 7) ^
+        // (row & 7) into physical chunk lane & 7 of its row
+        uint16_t* dx = (dst == sK0 ? sKx0 : sKx1) + wave * 512;
+        const int rowx = 8 * wave + (lane >> 3);
+        const int lcx = (lane & 7) ^ (rowx & 7);
+        const int rx = min(rowx, lim);            // rows past the last valid one read that row
+        if constexpr (!SPLIT) {
+          const char* tbx = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
+          dma16_buf_s<false>(tbx, (uint32_t)(rx * ES * rs + ES * D + 16 * lcx), 0u, dx);
+        } else if constexpr (PAGED) {
+          const int t = tb + rx;
+          const int page = clamp_page(a.table[(int64_t)b_t * a.max_pages + (t >> a.page_shift)], a.num_pages);
+          const char* src = reinterpret_cast<const char*>(kv_base) +
+                            ES * (paged_row(page, t & ((1 << a.page_shift) - 1), a.k_sb, rs) + D) + 16 * lcx;
+          dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dx);
+        } else {
+          const char* src = reinterpret_cast<const char*>(kv_base) + ES * ((int64_t)(tb + rx) * rs + D) + 16 * lcx;
+          dma16<SPLIT>(reinterpret_cast<const uint16_t*>(src), dx);
+        }
+      }
+    }
     if constexpr (!SPLIT) {
       // Prefill (dense K/V), buffer form: segment sg holds rows sg RPS ..
       // sg RPS + RPS - 1 of the tile; this lane fetches logical chunk lc of
@@ -508,6 +547,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   int mlen = 0;                // keys of the sequence (the mask is read below it)
   int ke = 0;                  // end (exclusive) of the keys the current tile may hold
   bf16x8 qf[NQC];
+  bf16x8 qfx[NQX];     // KX: this wave's share of the 64 extra query columns
   auto set_rows = [&](int b_, int g_, int rb_, int n_keys) {
     b = b_;
     const int rows = a.Sq * a.G;
@@ -541,6 +581,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const bool in_d = !kPad || 8 * hl + dh * (D / DS) + 16 * c < a.dk;
       if (row_ok && in_d) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
       qf[c] = as_bf16x8(w);
+    }
+    if constexpr (KX) {
+      // columns D + 16 (dh NQX + c) + 8 hl .. + 7
+      const int64_t qx = qoff - dh * (D / DS) + D + 16 * dh * NQX;
+#pragma unroll
+      for (int c = 0; c < NQX; ++c) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qx + 16 * c);
+        qfx[c] = as_bf16x8(w);
+      }
     }
   };
 
@@ -593,6 +643,21 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   float xscale = a.scale;    // the score scale of the score transform
   float vsc = 1.f;           // fp8 V: the KV head's V scale
 
+  // KX: this wave's NQX steps of the contraction over the extra key columns
+  // of the tile whose main part is in bk (row j, logical chunk 2 (dh NQX +
+  // c) + hl, stored at physical chunk lc ^ (row & 7))
+  auto score_extra = [&](const uint16_t* bk, f32x16& acc) {
+    if constexpr (KX) {
+      const uint16_t* bx = bk == sK0 ? sKx0 : sKx1;
+#pragma unroll
+      for (int c = 0; c < NQX; ++c) {
+        const int lc = 2 * (dh * NQX + c) + hl;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(&bx[j * DXK + 8 * (lc ^ (j & 7))]);
+        acc = mfma32(as_bf16x8(kw), qfx[c], acc);
+      }
+    }
+  };
+
   // S^T (this wave's part of the contraction) for the tile in bk
   auto scores = [&](const uint16_t* bk, f32x16 (&s)[NKB]) {
 #pragma unroll
@@ -616,6 +681,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         }
       }
     }
+    if constexpr (KX) score_extra(bk, s[0]);
   };
 
   // Mask values of the tile starting at key tb (MODS with a mask): for each
@@ -867,7 +933,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sX[slot][wave][kb * 16 + x][lane] = s[kb][x];
+        for (int x = 0; x < 16; ++x) sX[slot % XSLOTS][wave][kb * 16 + x][lane] = s[kb][x];
     }
   };
   auto combine_partner = [&](f32x16 (&s)[NKB], int slot) {
@@ -881,7 +947,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           if constexpr (DS == 2) {
-            const float other = sX[slot][wave ^ 1][kb * 16 + x][lane];
+            const float other = sX[slot % XSLOTS][wave ^ 1][kb * 16 + x][lane];
             s[kb][x] = dh == 0 ? s[kb][x] + other : other + s[kb][x];
           } else {
             float part[DS];
@@ -889,7 +955,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             for (int k = 0; k < DS; ++k) part[k] = s[kb][x];
 #pragma unroll
             for (int k = 0; k < DS; ++k)
-              if (k != dh) part[k] = sX[slot][w0 + k][kb * 16 + x][lane];
+              if (k != dh) part[k] = sX[slot % XSLOTS][w0 + k][kb * 16 + x][lane];
             float acc = part[0];
 #pragma unroll
             for (int k = 1; k < DS; ++k) acc += part[k];
@@ -1237,7 +1303,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       } else {
         // The copy order after the prologue is, per step t, V(t + NBUF - 1)
         // (refilling tile t-1's V buffer) then K(t + NBUF).
-        const bool deep = it + NBUF - 1 < n_loc;   // uniform: a full ring behind this tile
+        // uniform: a full ring behind this tile (the 576-wide-key kernel, whose
+        // K groups carry one more copy, waits for every copy instead)
+        const bool deep = !KX && it + NBUF - 1 < n_loc;
         // K(t) landed in every wave's share; every wave is done with the PV
         // product of tile t-1, whose V buffer is refilled next
         if (deep) wait_vm<AHEAD_CP>(); else wait_vm<0>();
@@ -1314,7 +1382,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // of one step (K(t+1+j), V(t+j)) form a group; the wait before step t
     // lets the groups issued after group t stay outstanding. Buffer indices
     // are compile-time constants in the unrolled ring.
-    constexpr int GROUP = 2 * SEGW;                         // copy instructions per group
+    constexpr int GROUP = 2 * SEGW + (KX ? 1 : 0);          // copy instructions per group
     constexpr bool kPrioMfma = D <= 128;
     constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
     constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
@@ -1345,7 +1413,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       if constexpr (kBig) {
         static_assert(DS == 2 && NKB == 1, "head dim 512: two waves share the scores of a 32-key tile");
 #pragma unroll
-        for (int x = 0; x < 16; ++x) oth[x] = sX[it & 1][wave ^ 1][x][lane];
+        for (int x = 0; x < 16; ++x) oth[x] = sX[(it & 1) % XSLOTS][wave ^ 1][x][lane];
       }
       load_mask(tb);
       if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
@@ -1422,6 +1490,12 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         }
         l_run += ls;
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KX) {
+          score_extra(bk, sn[0]);
+          // one exchange slot: every wave has read the partner's scores of
+          // tile t (at the top of this step) before any overwrites its slot
+          lds_barrier();
+        }
         publish(sn, (it + 1) & 1);
         // O^T += V^T P^T in batches of KB MFMAs, two transposing reads each
         constexpr int NPV = NKS * NDB;

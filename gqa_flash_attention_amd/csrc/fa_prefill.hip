@@ -46,6 +46,20 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   // 1 softcap / ALiBi, 2 with a mask; with head dims below D, 3 (no score
   // transform) or 4 (transform and mask)
   const bool xform = d.softcap > 0.f || d.max_bias > 0.f;
+  if constexpr (D == 512) {
+    if (d.dk > D) {
+      // 576-wide keys (the 512 tile plus 64 extra key columns): plain, or
+      // with the score transform and mask (softcap / ALiBi alone run with a
+      // null mask)
+      if (xform || d.mask != nullptr)
+        hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 2, false, true>),
+                           dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 0, false, true>),
+                           dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const int level = (d.dk < D || d.dv < D) ? (xform || d.mask != nullptr ? 4 : 3)
                     : d.mask != nullptr ? 2 : (xform ? 1 : 0);
   if (level == 4)

@@ -134,6 +134,20 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
   // the grid is what the chosen kernel holds resident
   static std::atomic<int> cache[2][5][kResidentDevs];
   cache_row = cache[paged][level];
+  if constexpr (D == 512) {
+    if (d.dk > D) {
+      // 576-wide keys: plain, or score transform and mask
+      static const K kernelsx[2][2] = {
+          {attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, 0, false, true>,
+           attn_kernel<D, NW, C::BN, C::DS, C::NBUF, false, true, C::WPE, 2, false, true>},
+          {attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 0, false, true>,
+           attn_kernel<D, NW, C::BN, C::DS, C::NBUF, true, true, C::WPE, 2, false, true>}};
+      static std::atomic<int> cachex[2][2][kResidentDevs];
+      const int lx = level == 0 ? 0 : 1;
+      k = kernelsx[paged][lx];
+      cache_row = cachex[paged][lx];
+    }
+  }
   if constexpr (D >= 128) {
     if (d.kv8) {
       // fp8 caches: plain, or score transform and mask (softcap / ALiBi alone

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad mask or scale, misaligned pointer */
-  FA_ERR_UNSUPPORTED = -2,  /* head dim not a multiple of 8 in [8, 512], page size not a power of two */
+  FA_ERR_UNSUPPORTED = -2,  /* head dims not multiples of 8 in [8, 512] (nor 576/512), page size not a power of two */
   FA_ERR_WORKSPACE = -3,    /* decode workspace missing or smaller than fa_decode_workspace_bytes */
   FA_ERR_LAUNCH = -4,       /* the HIP runtime rejected a kernel launch */
   FA_ERR_SCRATCH = -5       /* fa_decode_paged_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
@@ -124,9 +124,12 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
  *   contiguous copies of the same values.
  *   mods: host pointer to score modifiers (see fa_score_mods), NULL = none.
  *   Dk, Dv: the key and value head dims, which may differ (each a multiple
- *   of 8 in [8, 512]): q and k are [.., Dk], v and o [.., Dv]; the tile is
- *   the smallest of 64, 128, 256, 512 that holds both. fa_prefill is
- *   Dk = Dv = D.
+ *   of 8 in [8, 512], or the pair Dk = 576, Dv = 512): q and k are [.., Dk],
+ *   v and o [.., Dv]; the tile is the smallest of 64, 128, 256, 512 that
+ *   holds both (512 for 576/512: the 64 key columns past 512 are a small
+ *   tile of their own, taken in extra steps of the score contraction; the
+ *   FLASH_ATTN_EXT case grid of the llama.cpp PR 28507 report lists the
+ *   576/512 pair). FA_ERR_UNSUPPORTED otherwise. fa_prefill is Dk = Dv = D.
  */
 int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, const int64_t* k_stride,
                        const void* v, const int64_t* v_stride, void* o, const int64_t* o_stride,
@@ -137,7 +140,7 @@ int fa_prefill_strided(const void* q, const int64_t* q_stride, const void* k, co
  * Bytes of device workspace fa_decode_paged needs: fp32 partial outputs
  * [B, Hq, Sq, n_slots, W] and their LSEs [B, Hq, Sq, n_slots], with W the
  * tile width for head dim D (the smallest of 64, 128, 256, 512 that holds
- * it; with Dk != Dv pass the larger of the two), and
+ * it, 512 for D = 576; with Dk != Dv pass the larger of the two), and
  * n_slots = ceil(max_seq_len / kv_chunk) + 1 (a sequence's keys meet at most
  * that many workgroup ranges of the balanced split), each region 256-byte
  * aligned. Returns 0 for invalid sizes.

@@ -114,6 +114,9 @@ def test_workspace_bytes(lib):
     assert f(1, 1, 1, 64, 10, 48) == 0         # chunks are whole 32-key tiles
     # head dims below a tile width are sized at the tile width
     assert f(16, 1, 32, 80, 16384, 256) == f(16, 1, 32, 128, 16384, 256)
+    # 576-wide keys run on the 512 tile
+    assert f(2, 8, 16, 576, 4096, 256) == f(2, 8, 16, 512, 4096, 256)
+    assert f(2, 8, 16, 584, 4096, 256) == 0
     assert f(2, 3, 4, 320, 1000, 96) == f(2, 3, 4, 512, 1000, 96)
 
 
@@ -210,7 +213,8 @@ def test_score_mods_validation(lib):
 
 
 @pytest.mark.parametrize("dk,dv,want", [
-    (192, 128, OK), (320, 256, OK), (72, 80, OK), (8, 512, OK), (576, 512, UNSUPPORTED),
+    (192, 128, OK), (320, 256, OK), (72, 80, OK), (8, 512, OK), (576, 512, OK),
+    (576, 576, UNSUPPORTED), (576, 256, UNSUPPORTED), (584, 512, UNSUPPORTED), (512, 576, UNSUPPORTED),
     (128, 12, UNSUPPORTED), (0, 64, UNSUPPORTED),
 ])
 def test_dk_dv_validation(lib, dk, dv, want):

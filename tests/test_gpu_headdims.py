@@ -30,6 +30,11 @@ PREFILL = [
     (1, 90, 90, 4, 2, 320, 256, True, 0),
     (1, 64, 200, 4, 1, 40, 8, False, 0),
     (1, 70, 40, 4, 2, 112, 96, True, 0),            # Sq > Skv: leading rows see no key
+    # 576-wide keys with 512-wide values (the 512 tile plus 64 extra key columns)
+    (1, 150, 150, 8, 2, 576, 512, True, 0),
+    (2, 64, 200, 4, 1, 576, 512, True, 70),
+    (1, 70, 40, 4, 2, 576, 512, True, 0),
+    (1, 96, 96, 2, 2, 576, 512, False, 0),
 ]
 
 
@@ -102,6 +107,10 @@ DECODE = [
     (2, 1, 8, 2, 72, 72, 16, 640, [0, 639], 64, False),
     (2, 3, 8, 8, 96, 64, 16, 512, [300, 3], 96, False),
     (2, 2, 8, 2, 40, 40, 64, 256, [256, 100], 64, True),
+    (3, 1, 16, 4, 576, 512, 16, 1024, [1, 517, 1024], 256, True),
+    (2, 8, 16, 2, 576, 512, 16, 768, [8, 700], 128, True),   # 64 rows per KV head: two row blocks
+    (2, 3, 8, 8, 576, 512, 16, 512, [300, 3], 96, False),
+    (2, 2, 8, 2, 576, 512, 64, 256, [0, 200], 64, True),      # an empty sequence
 ]
 
 
@@ -190,3 +199,73 @@ def test_decode_padded_window():
     o_ref, lse_ref = oracle.attention_ref(q, torch.nan_to_num(kd.float()), torch.nan_to_num(vd.float()),
                                           causal=True, window=70, scale=scale, seq_lens=[640, 333])
     assert_parity(o, lse, o_ref, lse_ref, "decode 96/96 window 70")
+
+
+def test_wide_keys_modifiers_prefill_and_verify():
+    """576/512 with every score modifier (softcap, ALiBi, sinks, a mask with a
+    hidden band), in prefill (ragged, windowed) and in an 8-row verify over a
+    paged cache."""
+    Dk, Dv = 576, 512
+    g = torch.Generator().manual_seed(576)
+    B, S, Hq, Hkv = 1, 100, 4, 2
+    q, k, v = _randn(g, (B, S, Hq, Dk)), _randn(g, (B, S, Hkv, Dk)), _randn(g, (B, S, Hkv, Dv))
+    sinks = torch.randn(Hq, generator=g).float()
+    mask = (2.0 * torch.randn(B, S, S, generator=g)).to(torch.bfloat16)
+    mask[:, :, 10:14] = -float("inf")
+    kw = dict(softcap=20.0, max_bias=4.0)
+    scale = 1.0 / np.sqrt(Dk)
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, window=60, scale=scale,
+                        sinks=sinks.to(DEV), mask=mask.to(DEV), **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, causal=True, window=60, scale=scale,
+                                          sinks=sinks.double().numpy(), mask=mask, **kw)
+    assert_parity(o, lse, o_ref, lse_ref, "prefill 576/512 all modifiers")
+    B, Sq, Hq, Hkv, ps, L = 2, 8, 16, 2, 16, 512
+    q, kc, vc, table, lens_t, kd, vd = _decode_case(B, Sq, Hq, Hkv, Dk, Dv, ps, L, [L, 333], seed=577, paged=True)
+    sinks = torch.randn(Hq, generator=g).float()
+    mask = (2.0 * torch.randn(B, Sq, L, generator=g)).to(torch.bfloat16)
+    o, lse = fa.decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV), lens_t.to(DEV), page_size=ps,
+                             kv_chunk=128, causal=True, scale=scale, sinks=sinks.to(DEV), mask=mask.to(DEV), **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q, torch.nan_to_num(kd.float()), torch.nan_to_num(vd.float()),
+                                          causal=True, scale=scale, seq_lens=[L, 333],
+                                          sinks=sinks.double().numpy(), mask=mask, **kw)
+    assert_parity(o, lse, o_ref, lse_ref, "verify 576/512 all modifiers")
+
+
+def test_wide_keys_append_then_verify():
+    """fa_kv_append of 576-wide K and 512-wide V rows into a paged cache, then
+    an 8-row verify over it."""
+    Dk, Dv = 576, 512
+    B, Sq, Hq, Hkv, ps, L = 2, 8, 16, 2, 16, 384
+    q, kc, vc, table, lens_t, kd, vd = _decode_case(B, Sq, Hq, Hkv, Dk, Dv, ps, L, [L, 200], seed=578, paged=True)
+    g = torch.Generator().manual_seed(579)
+    kn, vn = _randn(g, (B, Sq, Hkv, Dk)), _randn(g, (B, Sq, Hkv, Dv))
+    kdev, vdev = kc.to(DEV), vc.to(DEV)
+    fa.kv_append(kdev, vdev, table.to(DEV), lens_t.to(DEV), kn.to(DEV), vn.to(DEV), page_size=ps)
+    o, lse = fa.decode_paged(q.to(DEV), kdev, vdev, table.to(DEV), lens_t.to(DEV), page_size=ps, kv_chunk=128,
+                             causal=True)
+    torch.cuda.synchronize()
+    for b, n in enumerate([L, 200]):
+        kd[b, n - Sq:n] = kn[b]
+        vd[b, n - Sq:n] = vn[b]
+    o_ref, lse_ref = oracle.attention_ref(q, torch.nan_to_num(kd.float()), torch.nan_to_num(vd.float()),
+                                          causal=True, scale=1.0 / np.sqrt(Dk), seq_lens=[L, 200])
+    assert_parity(o, lse, o_ref, lse_ref, "append + verify 576/512")
+
+
+def test_wide_keys_prefill_long_sampled():
+    """576/512 causal prefill over 2048 keys (64 tiles), sampled query rows
+    against the oracle."""
+    Dk, Dv = 576, 512
+    g = torch.Generator().manual_seed(580)
+    B, S, Hq, Hkv = 1, 2048, 4, 2
+    q, k, v = _randn(g, (B, S, Hq, Dk)), _randn(g, (B, S, Hkv, Dk)), _randn(g, (B, S, Hkv, Dv))
+    scale = 1.0 / np.sqrt(Dk)
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 777, 1500, 2046, 2047])
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, causal=True, scale=scale, rows=rows)
+    o_s = o[:, rows].cpu()
+    l_s = lse[:, :, rows].cpu()
+    assert_parity(o_s, l_s, o_ref[:, rows], lse_ref[:, :, rows], "prefill 576/512 S2048 sampled rows")

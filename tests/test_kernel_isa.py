@@ -27,8 +27,8 @@ import pytest
 
 from gqa_flash_attention_amd import build
 
-PREFILL_D128 = "_ZN5gqafa11attn_kernelILi128ELi4ELi64ELi1ELi2ELb0ELb0ELi2ELi0ELb0EEEvNS_8AttnArgsE"
-SPLIT_D128_PAGED_TWO_WAVES = "_ZN5gqafa11attn_kernelILi128ELi2ELi32ELi1ELi2ELb1ELb1ELi2ELi0ELb0EEEvNS_8AttnArgsE"
+PREFILL_D128 = "_ZN5gqafa11attn_kernelILi128ELi4ELi64ELi1ELi2ELb0ELb0ELi2ELi0ELb0ELb0EEEvNS_8AttnArgsE"
+SPLIT_D128_PAGED_TWO_WAVES = "_ZN5gqafa11attn_kernelILi128ELi2ELi32ELi1ELi2ELb1ELb1ELi2ELi0ELb0ELb0EEEvNS_8AttnArgsE"
 
 
 def _asm(src: str, out_dir: str) -> str:
