@@ -235,6 +235,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert((DS == 1 || DS == 2 || DS == 4) && NW % DS == 0, "a D split groups 2 or 4 waves");
   constexpr int BM = NW * 32 / DS;
+  // Prefill with eight full-D waves runs them as two groups in ping-pong
+  // (the main loop below); head dim 128 without score modifiers.
+  constexpr bool PP = !SPLIT && DS == 1 && NW == 8;
+  static_assert(!PP || (NBUF == 3 && BN == 64 && !KV8 && !KX && (MODS == 0 || MODS == 1)), "ping-pong prefill");
   // MODS level: 0 plain, 1 score transform (softcap, ALiBi), 2 transform +
   // mask, 3 plain with head dims below D, 4 transform + mask + head dims
   // below D
@@ -389,6 +393,34 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     tw_p0 = pf;
   };
 
+  // Prefill (dense K/V) copy of segment sg of one operand of the tile of
+  // keys [tb, tb + BN) into dst, buffer form: segment sg holds rows sg RPS ..
+  // sg RPS + RPS - 1 of the tile; this lane fetches logical chunk lc of row
+  // sg RPS + p_lr. The row part of the source offset is uniform (soffset);
+  // the lane part is one per-lane constant plus the chunk. (A few registers
+  // instead of three per segment: at head dim 512 the per-segment offsets
+  // left the main loop too few registers to keep more than one LDS operand
+  // read in flight.) With clamp_rows, rows past lim (the tile's last valid
+  // row) read that row instead: their scores are masked and their V rows
+  // get weight 0.
+  auto prefill_seg = [&](int tb, int lim, const uint16_t* kv_base, bool is_v, uint16_t* dst, int sg,
+                         bool clamp_rows) {
+    const int rs = is_v ? v_rs : k_rs;
+    const int rsb = ES * rs;                          // bytes per key row
+    const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
+    const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
+    uint32_t o = (is_v ? p_lrv : p_lrk) + 16u * (uint32_t)lc;
+    if (clamp_rows) {
+      const int r = sg * RPS + p_lr;
+      if (r > lim) o -= (uint32_t)((r - lim) * rsb);
+    }
+    if constexpr (kPad) {
+      // a chunk past the real head dim reads chunk 0 of the same row
+      if (8 * lc >= (is_v ? a.dv : a.dk)) o -= 16u * (uint32_t)lc;
+    }
+    dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
+  };
+
   // Copy one operand of the tile of keys [tb, tb + BN) of a sequence whose
   // keys end at ke_t (exclusive) into dst. kv_base is the K or V cache at
   // this KV head (and, for a contiguous cache, at this sequence). Keys past
@@ -425,13 +457,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       }
     }
     if constexpr (!SPLIT) {
-      // Prefill (dense K/V), buffer form: segment sg holds rows sg RPS ..
-      // sg RPS + RPS - 1 of the tile; this lane fetches logical chunk lc of
-      // row sg RPS + p_lr. The row part of the source offset is uniform
-      // (soffset); the lane part is one per-lane constant plus the chunk.
-      // (A few registers instead of three per segment: at head dim 512 the
-      // per-segment offsets left the main loop too few registers to keep
-      // more than one LDS operand read in flight.)
+      // one segment as prefill_seg above, with the tile's row base, row
+      // pitch and lane offset computed once for all segments
       const int rsb = ES * rs;                          // bytes per key row
       const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
       const uint32_t lro = is_v ? p_lrv : p_lrk;        // p_lr * rsb
@@ -440,13 +467,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
         uint32_t o = lro + 16u * (uint32_t)lc;
         if (clamp_rows) {
-          // rows past the last valid one read that row instead (their scores
-          // are masked, their V rows get weight 0)
           const int r = sg * RPS + p_lr;
           if (r > lim) o -= (uint32_t)((r - lim) * rsb);
         }
         if constexpr (kPad) {
-          // a chunk past the real head dim reads chunk 0 of the same row
           if (8 * lc >= (is_v ? a.dv : a.dk)) o -= 16u * (uint32_t)lc;
         }
         dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
@@ -1371,181 +1395,300 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, n_keys, kseq, bq, false, dst); };
     auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, n_keys, vseq, bq, true, dst); };
 
-    // ---- main loop, software-pipelined ---------------------------------------
-    // Step t: the scores of tile t are already in registers. After the
-    // barrier (tile t+1's K and tile t's V have landed in LDS, and every wave
-    // is done with step t-1), the wave starts the copies of K(t+NBUF) and
-    // V(t+NBUF-1) into the buffers step t-1 released, runs the S^T MFMAs of
-    // tile t+1 while the VALU exponentiates tile t, then accumulates O with
-    // tile t's V. The MFMA work of S(t+1) overlaps the softmax of tile t
-    // inside one wave, and NBUF-1 tiles of copies stay in flight. The copies
-    // of one step (K(t+1+j), V(t+j)) form a group; the wait before step t
-    // lets the groups issued after group t stay outstanding. Buffer indices
-    // are compile-time constants in the unrolled ring.
-    constexpr int GROUP = 2 * SEGW + (KX ? 1 : 0);          // copy instructions per group
-    constexpr bool kPrioMfma = D <= 128;
-    constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
-    constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
-    f32x16 sc[NKB];
-    if (n_tiles > 0) {
-      issue_k(t_start, kbuf(0));
+    if constexpr (PP) {
+      // ---- main loop, two wave groups in ping-pong -----------------------------
+      // Waves w and w + 4 share a SIMD. Group 0 (waves 0-3) holds rows 0-127
+      // of the block and group 1 rows 128-255; both read the same K/V tiles.
+      // Every wave runs the same program: the scores of tile 0, then per
+      // tile t a softmax slot (mask, max, exponentiate tile t) and an MFMA
+      // slot (the scores of tile t+1, then O += P V with tile t), each ended
+      // by a workgroup barrier. Group 1 passes one extra barrier first, so it
+      // runs one slot behind: while group 0 exponentiates, group 1 runs its
+      // MFMA block, and the other way round. Each SIMD then always has one
+      // wave feeding its matrix core and one on the VALU. (Measured on
+      // MI355X: a VALU wave beside an MFMA wave leaves the MFMA rate
+      // unchanged, while VALU work inside the MFMA wave's own stream slows
+      // it once there are more than ~4 VALU instructions per 32x32x16 MFMA;
+      // the softmax needs ~4.)
+      //
+      // Copies: a ring of three buffers per operand; every wave copies two
+      // 1 KiB segments of each tile of K and V. Issuing a copy stalls the
+      // issuing wave (the CU's vector memory unit takes ~10 cycles per 1 KiB
+      // copy, more under load: measured ~75 cycles per copy per wave), so
+      // the copies are split between the slots: in its softmax slot of tile
+      // t a wave copies its segments of K(t+2) into the buffer of K(t-1),
+      // and in its MFMA slot of tile t, between MFMAs, those of V(t+2) into
+      // the buffer of V(t-1); both buffers' last readers are the MFMA slots
+      // of the tile before, done by then in either group. At the end of its
+      // MFMA slot of tile t a wave waits until only that slot's two copies
+      // are in flight: for group 0 that covers K(t+2) (needed from the
+      // second slot of tile t+1 on) and V(t+1); for group 1, one slot behind,
+      // the same. Past the last tile the copies repeat the last tile into
+      // the same, free, buffers, so that every slot issues the same number
+      // of copies and the waits are exact (which also lets the compiler's
+      // own LDS hazard tracking see that no MFMA slot reads a buffer with a
+      // copy in flight).
+      static_assert(NBUF == 3 && SEGW == 2, "three tile buffers; two segments per wave and operand");
+      const int grp = wave >> 2;          // uniform
+      f32x16 sc[NKB];
+      u32x4 pf[NKS];
+      // this wave's two segments of one operand of the tile at key tb: as
+      // prefill_seg, with the clamp of rows past the sequence's end written
+      // without a branch (whole tiles subtract 0), so that the copies stay
+      // inside the MFMA slot's one basic block
+      auto copy2 = [&](int tb, const uint16_t* kv_base, bool is_v, uint16_t* dst) __attribute__((always_inline)) {
+        const int lim = n_keys - 1 - tb;
+        const int rs = is_v ? v_rs : k_rs;
+        const int rsb = ES * rs;
+        const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
 #pragma unroll
-      for (int jj = 0; jj < NBUF - 1; ++jj) {
-        if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
-        if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
-      }
-      if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
-      lds_barrier();
-      scores(kbuf(0), sc);
-      publish(sc, 0);
-    }
-    auto step = [&](int it, int u) {
-      const int tb = t_start + it * BN;
-      if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
-      lds_barrier();
-      // At head dim 512 (one wave per SIMD) the partner's scores are read
-      // first, so their LDS latency overlaps the copy issue below (measured:
-      // 1.79 -> 1.63 ms for the head-dim-512 causal workload; at head dim 256,
-      // two waves per SIMD, the other order is 2 % faster); they are added
-      // in once the first MFMAs of S(t+1) are under way.
-      constexpr bool kBig = D >= 512;
-      float oth[kBig ? 16 : 1];
-      if constexpr (kBig) {
-        static_assert(DS == 2 && NKB == 1, "head dim 512: two waves share the scores of a 32-key tile");
-#pragma unroll
-        for (int x = 0; x < 16; ++x) oth[x] = sX[(it & 1) % XSLOTS][wave ^ 1][x][lane];
-      }
-      load_mask(tb);
-      if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
-      if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
-      float nb = 0.f;
-      if constexpr (!kBig) {
-        combine_partner(sc, it & 1);
-        nb = prepare(sc, tb);
-      }
-      f32x16 sn[NKB];
-      // Up to D = 128 two workgroups share a CU, so each SIMD runs waves of
-      // both. A wave raises its priority for its MFMA block and drops it for
-      // the softmax bookkeeping and barrier that follow, so the issue
-      // arbiter feeds the matrix cores first (measured +2.4 % at head dim
-      // 128; with one workgroup per CU it gains nothing).
-      if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(1);
-      if constexpr (D >= 512) {
-        // Head dim 512 runs one wave per SIMD, so nothing covers a wave's
-        // own LDS latency, and its registers are too full for the compiler
-        // to keep more than one operand read in flight on its own. The step
-        // is written in explicit batches instead: the reads of the next
-        // batch are issued before the MFMAs of the current one (a schedule
-        // fence between batches); the first batch of S(t+1) is issued before
-        // tile t's exchange and softmax bookkeeping, which then run while it
-        // computes, and tile t's exponentiation is spread over the other
-        // S(t+1) batches.
-        const uint16_t* bk = kbuf((u + 1) % NBUF);
-        const uint16_t* bv = vbuf(u);
-        constexpr int KB = 4;                    // MFMAs per batch
-        constexpr int NSB = NQC / KB;            // S batches
-        constexpr int NPAIR = NKS * 4;           // exponentiated pairs per lane
-        static_assert(NKB == 1 && NQC % KB == 0 && (NKS * NDB) % KB == 0, "head dim 512 tile shape");
-        auto kread = [&](int c) -> u32x4 {
-          const int ch = 2 * (c + dh * NQC) + hl;
-          return *reinterpret_cast<const u32x4*>(&bk[j * D + 8 * (ch ^ swz_k<D>(j))]);
-        };
-        static_assert(NSB >= 2, "the exponentiation needs a batch after the first");
-        u32x4 kf[2][KB];
-#pragma unroll
-        for (int x = 0; x < KB; ++x) kf[0][x] = kread(x);
-        sn[0] = f32x16{};
-        u32x4 pf[NKS];
-        float ls = 0.f;
-#pragma unroll
-        for (int bi = 0; bi < NSB; ++bi) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (bi + 1 < NSB) {
-#pragma unroll
-            for (int x = 0; x < KB; ++x) kf[(bi + 1) & 1][x] = kread((bi + 1) * KB + x);
-          }
-#pragma unroll
-          for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
-          if (bi == 0) {
-            __builtin_amdgcn_sched_barrier(0);
-            // the partner's half of tile t's scores (same order in both
-            // waves, so the pair holds bit-identical sums), then the mask and
-            // the running max
-#pragma unroll
-            for (int x = 0; x < 16; ++x) sc[0][x] = dh == 0 ? sc[0][x] + oth[x] : oth[x] + sc[0][x];
-            nb = prepare(sc, tb);
-            continue;
-          }
-          // pairs q with q (NSB - 1) / NPAIR == bi - 1: an even share per
-          // batch after the first
-#pragma unroll
-          for (int q = 0; q < NPAIR; ++q) {
-            if (q * (NSB - 1) / NPAIR != bi - 1) continue;
-            const int ks = q / 4, w = q % 4, base = 8 * (ks & 1);
-            const float e0 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w], sl2, nb));
-            const float e1 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w + 1], sl2, nb));
-            ls += e0 + e1;
-            pf[ks][w] = pack_bf16(e0, e1);
-          }
+        for (int i = 0; i < SEGW; ++i) {
+          const int sg = wave * SEGW + i;
+          const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
+          const int over = max(sg * RPS + p_lr - lim, 0);
+          const uint32_t o = (is_v ? p_lrv : p_lrk) + 16u * (uint32_t)lc - (uint32_t)(over * rsb);
+          dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
         }
-        l_run += ls;
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (KX) {
-          score_extra(bk, sn[0]);
-          // one exchange slot: every wave has read the partner's scores of
-          // tile t (at the top of this step) before any overwrites its slot
-          lds_barrier();
-        }
-        publish(sn, (it + 1) & 1);
-        // O^T += V^T P^T in batches of KB MFMAs, two transposing reads each
-        constexpr int NPV = NKS * NDB;
-        auto vread = [&](int m, u32x4& out) {
-          const int ks = m / NDB, db = m % NDB;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
-            out[2 * half] = t[0];
-            out[2 * half + 1] = t[1];
-          }
-        };
-        u32x4 vf[2][KB];
-#pragma unroll
-        for (int x = 0; x < KB; ++x) vread(x, vf[0][x]);
-#pragma unroll
-        for (int bi = 0; bi < NPV / KB; ++bi) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (bi + 1 < NPV / KB) {
-#pragma unroll
-            for (int x = 0; x < KB; ++x) vread((bi + 1) * KB + x, vf[(bi + 1) & 1][x]);
-          }
-#pragma unroll
-          for (int x = 0; x < KB; ++x) {
-            const int m = bi * KB + x, ks = m / NDB, db = m % NDB;
-            oacc[db] = mfma32(as_bf16x8(vf[bi & 1][x]), as_bf16x8(pf[ks]), oacc[db]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
-        u32x4 pf[NKS];
+      };
+      // softmax slot of tile t (ring position u = t % 3), at raised
+      // priority: the issue arbiter then serves its VALU stream before the
+      // partner's MFMA and LDS issue (measured +0.6 %; raising the MFMA slot
+      // instead gained nothing)
+      auto vphase = [&](int t, int u) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        copy2(t_start + min(t + 2, n_tiles - 1) * BN, kseq, false, kbuf((u + 2) % 3));
+        const float nb = prepare(sc, t_start + t * BN);
         exponentiate(sc, nb, pf);
-        publish(sn, (it + 1) & 1);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) pin_vgpr(pf[ks]);
+        pin_vgpr(l_run);
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();
+      };
+      // MFMA slot of tile t: the next tile's scores (after the last tile, of
+      // whatever the buffer holds: unused), then O^T += V^T P^T with V(t)
+      auto mphase = [&](int t, int u) __attribute__((always_inline)) {
+        scores(kbuf((u + 1) % 3), sc);
+        copy2(t_start + min(t + 2, n_tiles - 1) * BN, vseq, true, vbuf((u + 2) % 3));
         accumulate(vbuf(u), pf);
-        // one schedule for the whole step: S(t+1) MFMAs each followed by the
-        // next K read and a share of tile t's exponentiation, then the PV
-        // MFMAs each followed by the next two V^T reads
-        sched_step<NKB * NQC, 1, NDB * NKS, 2, 4, kExpValuPerTile / (NKB * NQC)>();
-      }
-      if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        sched_phase_copies<NKB * NQC, 1, 4, 3, 9, 0>();
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        sched_phase<NDB * NKS, 2, 4, 0, 0>();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
-    };
-    for (int it = 0; it < n_tiles; it += NBUF) {
+        for (int kb = 0; kb < NKB; ++kb) pin_vgpr(sc[kb]);
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        if (it + u >= n_tiles) break;
-        step(it + u, u);
+        for (int db = 0; db < NDB; ++db) pin_vgpr(oacc[db]);
+        wait_vm<SEGW>();
+        lds_barrier();
+      };
+      if (n_tiles > 0) {
+        issue_k(t_start, kbuf(0));
+        issue_v(t_start, vbuf(0));
+        if (n_tiles > 1) {
+          issue_k(t_start + BN, kbuf(1));
+          issue_v(t_start + BN, vbuf(1));
+        }
+        wait_vm<0>();
+        lds_barrier();
+        if (grp == 1) lds_barrier();      // group 1: one slot behind
+        scores(kbuf(0), sc);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) pin_vgpr(sc[kb]);
+        lds_barrier();
+        for (int t = 0; t < n_tiles; t += 3) {
+          vphase(t, 0);
+          mphase(t, 0);
+          if (t + 1 < n_tiles) {
+            vphase(t + 1, 1);
+            mphase(t + 1, 1);
+          }
+          if (t + 2 < n_tiles) {
+            vphase(t + 2, 2);
+            mphase(t + 2, 2);
+          }
+        }
+        wait_vm<0>();                     // no copy lands in the staging below
+        if (grp == 0) lds_barrier();      // matches group 1's extra barrier
       }
+    } else {
+      // ---- main loop, software-pipelined ---------------------------------------
+      // Step t: the scores of tile t are already in registers. After the
+      // barrier (tile t+1's K and tile t's V have landed in LDS, and every wave
+      // is done with step t-1), the wave starts the copies of K(t+NBUF) and
+      // V(t+NBUF-1) into the buffers step t-1 released, runs the S^T MFMAs of
+      // tile t+1 while the VALU exponentiates tile t, then accumulates O with
+      // tile t's V. The MFMA work of S(t+1) overlaps the softmax of tile t
+      // inside one wave, and NBUF-1 tiles of copies stay in flight. The copies
+      // of one step (K(t+1+j), V(t+j)) form a group; the wait before step t
+      // lets the groups issued after group t stay outstanding. Buffer indices
+      // are compile-time constants in the unrolled ring.
+      constexpr int GROUP = 2 * SEGW + (KX ? 1 : 0);          // copy instructions per group
+      constexpr bool kPrioMfma = D <= 128;
+      constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
+      constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
+      f32x16 sc[NKB];
+      if (n_tiles > 0) {
+        issue_k(t_start, kbuf(0));
+  #pragma unroll
+        for (int jj = 0; jj < NBUF - 1; ++jj) {
+          if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
+          if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
+        }
+        if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
+        lds_barrier();
+        scores(kbuf(0), sc);
+        publish(sc, 0);
+      }
+      auto step = [&](int it, int u) {
+        const int tb = t_start + it * BN;
+        if (it + NBUF - 1 < n_tiles) wait_vm<LATER_STEP>(); else wait_vm<0>();
+        lds_barrier();
+        // At head dim 512 (one wave per SIMD) the partner's scores are read
+        // first, so their LDS latency overlaps the copy issue below (measured:
+        // 1.79 -> 1.63 ms for the head-dim-512 causal workload; at head dim 256,
+        // two waves per SIMD, the other order is 2 % faster); they are added
+        // in once the first MFMAs of S(t+1) are under way.
+        constexpr bool kBig = D >= 512;
+        float oth[kBig ? 16 : 1];
+        if constexpr (kBig) {
+          static_assert(DS == 2 && NKB == 1, "head dim 512: two waves share the scores of a 32-key tile");
+  #pragma unroll
+          for (int x = 0; x < 16; ++x) oth[x] = sX[(it & 1) % XSLOTS][wave ^ 1][x][lane];
+        }
+        load_mask(tb);
+        if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
+        if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
+        float nb = 0.f;
+        if constexpr (!kBig) {
+          combine_partner(sc, it & 1);
+          nb = prepare(sc, tb);
+        }
+        f32x16 sn[NKB];
+        // Up to D = 128 two workgroups share a CU, so each SIMD runs waves of
+        // both. A wave raises its priority for its MFMA block and drops it for
+        // the softmax bookkeeping and barrier that follow, so the issue
+        // arbiter feeds the matrix cores first (measured +2.4 % at head dim
+        // 128; with one workgroup per CU it gains nothing).
+        if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(1);
+        if constexpr (D >= 512) {
+          // Head dim 512 runs one wave per SIMD, so nothing covers a wave's
+          // own LDS latency, and its registers are too full for the compiler
+          // to keep more than one operand read in flight on its own. The step
+          // is written in explicit batches instead: the reads of the next
+          // batch are issued before the MFMAs of the current one (a schedule
+          // fence between batches); the first batch of S(t+1) is issued before
+          // tile t's exchange and softmax bookkeeping, which then run while it
+          // computes, and tile t's exponentiation is spread over the other
+          // S(t+1) batches.
+          const uint16_t* bk = kbuf((u + 1) % NBUF);
+          const uint16_t* bv = vbuf(u);
+          constexpr int KB = 4;                    // MFMAs per batch
+          constexpr int NSB = NQC / KB;            // S batches
+          constexpr int NPAIR = NKS * 4;           // exponentiated pairs per lane
+          static_assert(NKB == 1 && NQC % KB == 0 && (NKS * NDB) % KB == 0, "head dim 512 tile shape");
+          auto kread = [&](int c) -> u32x4 {
+            const int ch = 2 * (c + dh * NQC) + hl;
+            return *reinterpret_cast<const u32x4*>(&bk[j * D + 8 * (ch ^ swz_k<D>(j))]);
+          };
+          static_assert(NSB >= 2, "the exponentiation needs a batch after the first");
+          u32x4 kf[2][KB];
+  #pragma unroll
+          for (int x = 0; x < KB; ++x) kf[0][x] = kread(x);
+          sn[0] = f32x16{};
+          u32x4 pf[NKS];
+          float ls = 0.f;
+  #pragma unroll
+          for (int bi = 0; bi < NSB; ++bi) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 1 < NSB) {
+  #pragma unroll
+              for (int x = 0; x < KB; ++x) kf[(bi + 1) & 1][x] = kread((bi + 1) * KB + x);
+            }
+  #pragma unroll
+            for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
+            if (bi == 0) {
+              __builtin_amdgcn_sched_barrier(0);
+              // the partner's half of tile t's scores (same order in both
+              // waves, so the pair holds bit-identical sums), then the mask and
+              // the running max
+  #pragma unroll
+              for (int x = 0; x < 16; ++x) sc[0][x] = dh == 0 ? sc[0][x] + oth[x] : oth[x] + sc[0][x];
+              nb = prepare(sc, tb);
+              continue;
+            }
+            // pairs q with q (NSB - 1) / NPAIR == bi - 1: an even share per
+            // batch after the first
+  #pragma unroll
+            for (int q = 0; q < NPAIR; ++q) {
+              if (q * (NSB - 1) / NPAIR != bi - 1) continue;
+              const int ks = q / 4, w = q % 4, base = 8 * (ks & 1);
+              const float e0 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w], sl2, nb));
+              const float e1 = fast_exp2(fmaf(sc[ks >> 1][base + 2 * w + 1], sl2, nb));
+              ls += e0 + e1;
+              pf[ks][w] = pack_bf16(e0, e1);
+            }
+          }
+          l_run += ls;
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (KX) {
+            score_extra(bk, sn[0]);
+            // one exchange slot: every wave has read the partner's scores of
+            // tile t (at the top of this step) before any overwrites its slot
+            lds_barrier();
+          }
+          publish(sn, (it + 1) & 1);
+          // O^T += V^T P^T in batches of KB MFMAs, two transposing reads each
+          constexpr int NPV = NKS * NDB;
+          auto vread = [&](int m, u32x4& out) {
+            const int ks = m / NDB, db = m % NDB;
+  #pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
+              out[2 * half] = t[0];
+              out[2 * half + 1] = t[1];
+            }
+          };
+          u32x4 vf[2][KB];
+  #pragma unroll
+          for (int x = 0; x < KB; ++x) vread(x, vf[0][x]);
+  #pragma unroll
+          for (int bi = 0; bi < NPV / KB; ++bi) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 1 < NPV / KB) {
+  #pragma unroll
+              for (int x = 0; x < KB; ++x) vread((bi + 1) * KB + x, vf[(bi + 1) & 1][x]);
+            }
+  #pragma unroll
+            for (int x = 0; x < KB; ++x) {
+              const int m = bi * KB + x, ks = m / NDB, db = m % NDB;
+              oacc[db] = mfma32(as_bf16x8(vf[bi & 1][x]), as_bf16x8(pf[ks]), oacc[db]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
+          u32x4 pf[NKS];
+          exponentiate(sc, nb, pf);
+          publish(sn, (it + 1) & 1);
+          accumulate(vbuf(u), pf);
+          // one schedule for the whole step: S(t+1) MFMAs each followed by the
+          // next K read and a share of tile t's exponentiation, then the PV
+          // MFMAs each followed by the next two V^T reads
+          sched_step<NKB * NQC, 1, NDB * NKS, 2, 4, kExpValuPerTile / (NKB * NQC)>();
+        }
+        if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+      };
+      for (int it = 0; it < n_tiles; it += NBUF) {
+  #pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          if (it + u >= n_tiles) break;
+          step(it + u, u);
+        }
+      }
+
     }
 
     // ---- epilogue ------------------------------------------------------------
@@ -1592,7 +1735,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       // tile; 16-byte chunks XOR-swizzled by the row) and written back 16 bytes
       // per lane, a row's chunks in consecutive lanes.
       constexpr int CH = D / 8;                 // 16-byte chunks per row
-      static_assert(BM <= 4 * BN && NBUF == 2, "the staged block fits the four tile buffers");
+      static_assert(BM <= 4 * BN && NBUF >= 2, "the staged block fits four tile buffers");
       auto stage = [&](int row) -> uint16_t* {
         const int r = row % BN;
         uint16_t* base = row < BN ? sK0 : row < 2 * BN ? sK1 : row < 3 * BN ? sV0 : sV1;

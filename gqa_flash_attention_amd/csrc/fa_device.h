@@ -127,6 +127,20 @@ __device__ __forceinline__ void sched_phase() {
     sched_phase<N, R, AHEAD, V, I + 1>();
   }
 }
+// As sched_phase, with one vector memory instruction (a tile copy) placed
+// after MFMA number C1 and one after MFMA number C2.
+template <int N, int R, int AHEAD, int C1, int C2, int I>
+__device__ __forceinline__ void sched_phase_copies() {
+  if constexpr (I < N) {
+    constexpr int total = N * R;
+    constexpr int lo = I * R + AHEAD < total ? I * R + AHEAD : total;
+    constexpr int hi = (I + 1) * R + AHEAD < total ? (I + 1) * R + AHEAD : total;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);
+    if constexpr (I == C1 || I == C2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    sched_phase_copies<N, R, AHEAD, C1, C2, I + 1>();
+  }
+}
 template <int N1, int R1, int N2, int R2, int AHEAD, int V1>
 __device__ __forceinline__ void sched_step() {
   constexpr int a1 = AHEAD < N1 * R1 ? AHEAD : N1 * R1;
@@ -168,6 +182,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+
+// Holds a value in VGPRs at this point of the program: the value must be
+// computed before it, and code after it sees the pinned copy. With it, pure
+// arithmetic (exponentials, MFMAs) cannot be moved across the barrier that
+// follows by the compiler, which orders only memory accesses around one.
+template <typename T>
+__device__ __forceinline__ void pin_vgpr(T& x) {
+  asm volatile("" : "+v"(x));
+}
 
 // Transposing LDS read of four 16-bit values (ds_read_b64_tr_b16). Within
 // each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows

@@ -62,6 +62,17 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
   }
   const int level = (d.dk < D || d.dv < D) ? (xform || d.mask != nullptr ? 4 : 3)
                     : d.mask != nullptr ? 2 : (xform ? 1 : 0);
+  if constexpr (D == 128) {
+    if (level == 0) {
+      // eight waves in two ping-pong groups, 256 rows per workgroup
+      constexpr int kWaves = 8;
+      a.n_rb = (int)((rows + kWaves * 32 - 1) / (kWaves * 32));
+      const int64_t grid_pp = (int64_t)d.B * d.Hkv * a.n_rb;
+      hipLaunchKernelGGL((attn_kernel<D, kWaves, 64, 1, 3, false, false, 2, 0>), dim3((unsigned)grid_pp),
+                         dim3(kWaves * 64), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (level == 4)
     hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 4>), dim3((unsigned)grid),
                        dim3(C::NW * 64), 0, stream, a);

@@ -37,6 +37,12 @@ GRID = [
     (1, 129, 129, 8, 1, 64, 1, 0),
     (1, 520, 520, 2, 2, 256, 1, 200),
     (1, 96, 160, 4, 2, 512, 1, 33),
+    # head dim 128 without modifiers runs two wave groups in ping-pong over a
+    # ring of three tile buffers: tile counts of every residue mod 3, long
+    # windows, non-causal ragged keys, many query heads per KV head
+    (1, 700, 700, 8, 2, 128, 1, 300),
+    (1, 300, 333, 2, 2, 128, 0, 0),
+    (1, 65, 65, 16, 1, 128, 1, 0),
 ]
 
 

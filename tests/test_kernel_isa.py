@@ -9,6 +9,11 @@ to gfx950 assembly with the library's own flags and check the hot blocks:
   `s_waitcnt vmcnt(0)` — its tile copies stay in flight until the next
   step's explicit wait — and its LDS operand waits are graded (some
   `lgkmcnt(N)` with N > 0), so operand reads issued ahead stay in flight;
+* in the head-dim-128 prefill (two wave groups in ping-pong) each block
+  holding a softmax slot and an MFMA slot keeps them apart: every
+  exponential before the slot barrier, every MFMA after it (the compiler
+  is free to move arithmetic across a barrier; explicit register pins stop
+  it);
 * the split-KV loop that keeps its copy ring full (two waves over a paged
   cache, the verify shape) reads no tile right behind a full drain
   (`s_waitcnt vmcnt(0) lgkmcnt(0)` in front of a `ds_read`): each tile read
@@ -27,7 +32,8 @@ import pytest
 
 from gqa_flash_attention_amd import build
 
-PREFILL_D128 = "_ZN5gqafa11attn_kernelILi128ELi4ELi64ELi1ELi2ELb0ELb0ELi2ELi0ELb0ELb0EEEvNS_8AttnArgsE"
+PREFILL_D128 = "_ZN5gqafa11attn_kernelILi128ELi8ELi64ELi1ELi3ELb0ELb0ELi2ELi0ELb0ELb0EEEvNS_8AttnArgsE"
+PREFILL_D128_MASK = "_ZN5gqafa11attn_kernelILi128ELi4ELi64ELi1ELi2ELb0ELb0ELi2ELi2ELb0ELb0EEEvNS_8AttnArgsE"
 SPLIT_D128_PAGED_TWO_WAVES = "_ZN5gqafa11attn_kernelILi128ELi2ELi32ELi1ELi2ELb1ELb1ELi2ELi0ELb0ELb0EEEvNS_8AttnArgsE"
 
 
@@ -89,8 +95,9 @@ def _loop(body: list[str]) -> list[str]:
     return body[best[0]:best[1] + 1]
 
 
-def test_prefill_main_block_keeps_copies_and_reads_in_flight(asm):
-    blocks = [b for b in _blocks(_function(asm["prefill"], PREFILL_D128))
+@pytest.mark.parametrize("kernel", [PREFILL_D128, PREFILL_D128_MASK], ids=["ping_pong", "masked"])
+def test_prefill_main_block_keeps_copies_and_reads_in_flight(asm, kernel):
+    blocks = [b for b in _blocks(_function(asm["prefill"], kernel))
               if sum(i.startswith("v_mfma") for i in b) >= 32]
     assert blocks, "prefill main block (32 MFMAs) not found"
     for b in blocks:
@@ -99,6 +106,19 @@ def test_prefill_main_block_keeps_copies_and_reads_in_flight(asm):
             "a tile-copy drain inside the prefill main block"
         graded = [w for w in waits if re.search(r"lgkmcnt\(([1-9]\d*)\)", w)]
         assert graded, "prefill operand reads wait for all LDS reads (lgkmcnt(0) only)"
+
+
+def test_ping_pong_slots_stay_apart(asm):
+    blocks = [b for b in _blocks(_function(asm["prefill"], PREFILL_D128))
+              if sum(i.startswith("v_mfma") for i in b) >= 32 and sum(i.startswith("v_exp") for i in b) >= 32]
+    assert len(blocks) == 3, "one softmax + MFMA block per ring position expected"
+    for b in blocks:
+        bar = [k for k, i in enumerate(b) if i.startswith("s_barrier")]
+        exps = [k for k, i in enumerate(b) if i.startswith("v_exp")]
+        mfma = [k for k, i in enumerate(b) if i.startswith("v_mfma")]
+        assert len(bar) >= 1, "no slot barrier inside the block"
+        assert max(exps) < bar[0] < min(mfma), "softmax and MFMA work mixed across the slot barrier"
+        assert all(max(mfma) < k for k in bar[1:]), "MFMA work after the MFMA slot's closing barrier"
 
 
 def test_split_loop_reads_tiles_without_full_drain(asm):
