@@ -397,27 +397,22 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // keys [tb, tb + BN) into dst, buffer form: segment sg holds rows sg RPS ..
   // sg RPS + RPS - 1 of the tile; this lane fetches logical chunk lc of row
   // sg RPS + p_lr. The row part of the source offset is uniform (soffset);
-  // the lane part is one per-lane constant plus the chunk. (A few registers
-  // instead of three per segment: at head dim 512 the per-segment offsets
-  // left the main loop too few registers to keep more than one LDS operand
-  // read in flight.) With clamp_rows, rows past lim (the tile's last valid
-  // row) read that row instead: their scores are masked and their V rows
-  // get weight 0.
-  auto prefill_seg = [&](int tb, int lim, const uint16_t* kv_base, bool is_v, uint16_t* dst, int sg,
-                         bool clamp_rows) {
+  // the lane part is one per-lane constant plus the chunk. Rows at or past
+  // ke_t, the sequence's end, read its last key's row (their
+  // scores are masked, their V rows get weight 0), and for head dims below
+  // D a chunk past the real one reads chunk 0 of its row; both are written
+  // without branches (whole tiles subtract 0), so copies placed between
+  // MFMAs stay in the MFMA block's one basic block.
+  auto prefill_seg = [&](int tb, int ke_t, const uint16_t* kv_base, bool is_v, uint16_t* dst, int sg)
+      __attribute__((always_inline)) {
+    const int lim = ke_t - 1 - tb;
     const int rs = is_v ? v_rs : k_rs;
     const int rsb = ES * rs;                          // bytes per key row
     const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
     const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
-    uint32_t o = (is_v ? p_lrv : p_lrk) + 16u * (uint32_t)lc;
-    if (clamp_rows) {
-      const int r = sg * RPS + p_lr;
-      if (r > lim) o -= (uint32_t)((r - lim) * rsb);
-    }
-    if constexpr (kPad) {
-      // a chunk past the real head dim reads chunk 0 of the same row
-      if (8 * lc >= (is_v ? a.dv : a.dk)) o -= 16u * (uint32_t)lc;
-    }
+    const int over = max(sg * RPS + p_lr - lim, 0);
+    uint32_t o = (is_v ? p_lrv : p_lrk) + 16u * (uint32_t)lc - (uint32_t)(over * rsb);
+    if constexpr (kPad) o -= 8 * lc >= (is_v ? a.dv : a.dk) ? 16u * (uint32_t)lc : 0u;
     dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
   };
 
@@ -1432,23 +1427,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const int grp = wave >> 2;          // uniform
       f32x16 sc[NKB];
       u32x4 pf[NKS];
-      // this wave's two segments of one operand of the tile at key tb: as
-      // prefill_seg, with the clamp of rows past the sequence's end written
-      // without a branch (whole tiles subtract 0), so that the copies stay
-      // inside the MFMA slot's one basic block
+      // this wave's two segments of one operand of the tile at key tb
       auto copy2 = [&](int tb, const uint16_t* kv_base, bool is_v, uint16_t* dst) __attribute__((always_inline)) {
-        const int lim = n_keys - 1 - tb;
-        const int rs = is_v ? v_rs : k_rs;
-        const int rsb = ES * rs;
-        const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)ES * tb * rs;
 #pragma unroll
-        for (int i = 0; i < SEGW; ++i) {
-          const int sg = wave * SEGW + i;
-          const int lc = is_v ? p_vchunk(sg) : p_kchunk(sg);
-          const int over = max(sg * RPS + p_lr - lim, 0);
-          const uint32_t o = (is_v ? p_lrv : p_lrk) + 16u * (uint32_t)lc - (uint32_t)(over * rsb);
-          dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
-        }
+        for (int i = 0; i < SEGW; ++i) prefill_seg(tb, n_keys, kv_base, is_v, dst, wave * SEGW + i);
       };
       // softmax slot of tile t (ring position u = t % 3), at raised
       // priority: the issue arbiter then serves its VALU stream before the
@@ -1530,7 +1512,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       f32x16 sc[NKB];
       if (n_tiles > 0) {
         issue_k(t_start, kbuf(0));
-  #pragma unroll
+#pragma unroll
         for (int jj = 0; jj < NBUF - 1; ++jj) {
           if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
           if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
@@ -1550,15 +1532,26 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // two waves per SIMD, the other order is 2 % faster); they are added
         // in once the first MFMAs of S(t+1) are under way.
         constexpr bool kBig = D >= 512;
+        // At head dim 512 (one wave per SIMD, 16 copies per wave and step)
+        // the copies go out two at a time after each batch of MFMAs: issuing
+        // a copy stalls the issuing wave (measured ~75 cycles per copy with
+        // several waves of a CU issuing), and issued at the top of the step
+        // the 16 stalls left the matrix cores idle. Past the last tile the
+        // copies repeat the last tile into the same free buffers, so every
+        // step issues the same copies and the waits stay exact; the 576-wide
+        // key tiles keep the copies at the top of the step.
+        constexpr bool kCopyBatched = kBig && !KX;
         float oth[kBig ? 16 : 1];
         if constexpr (kBig) {
           static_assert(DS == 2 && NKB == 1, "head dim 512: two waves share the scores of a 32-key tile");
-  #pragma unroll
+#pragma unroll
           for (int x = 0; x < 16; ++x) oth[x] = sX[(it & 1) % XSLOTS][wave ^ 1][x][lane];
         }
         load_mask(tb);
-        if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
-        if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
+        if constexpr (!kCopyBatched) {
+          if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
+          if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
+        }
         float nb = 0.f;
         if constexpr (!kBig) {
           combine_partner(sc, it & 1);
@@ -1592,34 +1585,46 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             return *reinterpret_cast<const u32x4*>(&bk[j * D + 8 * (ch ^ swz_k<D>(j))]);
           };
           static_assert(NSB >= 2, "the exponentiation needs a batch after the first");
+          static_assert(NBUF == 2 && SEGW % NSB == 0 && SEGW % ((NKS * NDB) / KB) == 0, "copies per batch");
+          auto copies = [&](int bi, bool is_v, int nb_batches) __attribute__((always_inline)) {
+            if constexpr (kCopyBatched) {
+              const int per = SEGW / nb_batches;
+              const int tc = t_start + min(it + (is_v ? 1 : 2), n_tiles - 1) * BN;
+#pragma unroll
+              for (int x = 0; x < per; ++x)
+                prefill_seg(tc, n_keys, is_v ? vseq : kseq, is_v, is_v ? vbuf(u ^ 1) : kbuf(u),
+                            wave * SEGW + bi * per + x);
+            }
+          };
           u32x4 kf[2][KB];
-  #pragma unroll
+#pragma unroll
           for (int x = 0; x < KB; ++x) kf[0][x] = kread(x);
           sn[0] = f32x16{};
           u32x4 pf[NKS];
           float ls = 0.f;
-  #pragma unroll
+#pragma unroll
           for (int bi = 0; bi < NSB; ++bi) {
             __builtin_amdgcn_sched_barrier(0);
             if (bi + 1 < NSB) {
-  #pragma unroll
+#pragma unroll
               for (int x = 0; x < KB; ++x) kf[(bi + 1) & 1][x] = kread((bi + 1) * KB + x);
             }
-  #pragma unroll
+#pragma unroll
             for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
+            copies(bi, false, NSB);
             if (bi == 0) {
               __builtin_amdgcn_sched_barrier(0);
               // the partner's half of tile t's scores (same order in both
               // waves, so the pair holds bit-identical sums), then the mask and
               // the running max
-  #pragma unroll
+#pragma unroll
               for (int x = 0; x < 16; ++x) sc[0][x] = dh == 0 ? sc[0][x] + oth[x] : oth[x] + sc[0][x];
               nb = prepare(sc, tb);
               continue;
             }
             // pairs q with q (NSB - 1) / NPAIR == bi - 1: an even share per
             // batch after the first
-  #pragma unroll
+#pragma unroll
             for (int q = 0; q < NPAIR; ++q) {
               if (q * (NSB - 1) / NPAIR != bi - 1) continue;
               const int ks = q / 4, w = q % 4, base = 8 * (ks & 1);
@@ -1642,7 +1647,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           constexpr int NPV = NKS * NDB;
           auto vread = [&](int m, u32x4& out) {
             const int ks = m / NDB, db = m % NDB;
-  #pragma unroll
+#pragma unroll
             for (int half = 0; half < 2; ++half) {
               const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
               out[2 * half] = t[0];
@@ -1650,20 +1655,21 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             }
           };
           u32x4 vf[2][KB];
-  #pragma unroll
+#pragma unroll
           for (int x = 0; x < KB; ++x) vread(x, vf[0][x]);
-  #pragma unroll
+#pragma unroll
           for (int bi = 0; bi < NPV / KB; ++bi) {
             __builtin_amdgcn_sched_barrier(0);
             if (bi + 1 < NPV / KB) {
-  #pragma unroll
+#pragma unroll
               for (int x = 0; x < KB; ++x) vread((bi + 1) * KB + x, vf[(bi + 1) & 1][x]);
             }
-  #pragma unroll
+#pragma unroll
             for (int x = 0; x < KB; ++x) {
               const int m = bi * KB + x, ks = m / NDB, db = m % NDB;
               oacc[db] = mfma32(as_bf16x8(vf[bi & 1][x]), as_bf16x8(pf[ks]), oacc[db]);
             }
+            copies(bi, true, NPV / KB);
           }
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -1678,16 +1684,17 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           sched_step<NKB * NQC, 1, NDB * NKS, 2, 4, kExpValuPerTile / (NKB * NQC)>();
         }
         if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
       };
       for (int it = 0; it < n_tiles; it += NBUF) {
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < NBUF; ++u) {
           if (it + u >= n_tiles) break;
           step(it + u, u);
         }
       }
+      if constexpr (D >= 512 && !KX) wait_vm<0>();   // the repeated copies after the last tile
 
     }
 
