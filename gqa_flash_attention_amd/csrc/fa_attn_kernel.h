@@ -1506,6 +1506,26 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       // lets the groups issued after group t stay outstanding. Buffer indices
       // are compile-time constants in the unrolled ring.
       constexpr int GROUP = 2 * SEGW + (KX ? 1 : 0);          // copy instructions per group
+      // Where a step issues its copies. Issuing a copy stalls the issuing
+      // wave (measured ~40-75 cycles per copy with several waves of a CU
+      // issuing), so the copies go where the stall hides best:
+      // * head dim 512 (one wave per SIMD, 16 copies per wave and step):
+      //   after the first two batches of MFMAs, eight after each. At the
+      //   top of the step the stalls left the matrix cores idle, and copies
+      //   spread to the end of the step made the next step wait for them
+      //   (measured, C4B: top of the step 1.61 ms, two after every batch
+      //   1.58, four after each score batch 1.55, eight after each of the
+      //   first two 1.47-1.52);
+      // * head dim 256: inside the MFMA block, after the scores' MFMAs are
+      //   issued (C4A 0.215 -> 0.205 ms; after the softmax bookkeeping
+      //   instead: no change);
+      // * otherwise, and for 576-wide key tiles: at the top of the step.
+      // The first two place copies with the branch-free segment copy and,
+      // past the last tile, repeat the last tile into the same free
+      // buffers, so every step issues the same copies and the waits stay
+      // exact; a last wait after the loop drains them.
+      constexpr bool kCopyBatched = D >= 512 && !KX;
+      constexpr bool kCopyInBlock = D == 256;
       constexpr bool kPrioMfma = D <= 128;
       constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
       constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
@@ -1532,15 +1552,6 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         // two waves per SIMD, the other order is 2 % faster); they are added
         // in once the first MFMAs of S(t+1) are under way.
         constexpr bool kBig = D >= 512;
-        // At head dim 512 (one wave per SIMD, 16 copies per wave and step)
-        // the copies go out two at a time after each batch of MFMAs: issuing
-        // a copy stalls the issuing wave (measured ~75 cycles per copy with
-        // several waves of a CU issuing), and issued at the top of the step
-        // the 16 stalls left the matrix cores idle. Past the last tile the
-        // copies repeat the last tile into the same free buffers, so every
-        // step issues the same copies and the waits stay exact; the 576-wide
-        // key tiles keep the copies at the top of the step.
-        constexpr bool kCopyBatched = kBig && !KX;
         float oth[kBig ? 16 : 1];
         if constexpr (kBig) {
           static_assert(DS == 2 && NKB == 1, "head dim 512: two waves share the scores of a 32-key tile");
@@ -1548,7 +1559,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           for (int x = 0; x < 16; ++x) oth[x] = sX[(it & 1) % XSLOTS][wave ^ 1][x][lane];
         }
         load_mask(tb);
-        if constexpr (!kCopyBatched) {
+        if constexpr (!kCopyBatched && !kCopyInBlock) {
           if (it + NBUF < n_tiles) issue_k(tb + NBUF * BN, kbuf(u));
           if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
         }
@@ -1585,7 +1596,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             return *reinterpret_cast<const u32x4*>(&bk[j * D + 8 * (ch ^ swz_k<D>(j))]);
           };
           static_assert(NSB >= 2, "the exponentiation needs a batch after the first");
-          static_assert(NBUF == 2 && SEGW % NSB == 0 && SEGW % ((NKS * NDB) / KB) == 0, "copies per batch");
+          static_assert(NBUF == 2 && SEGW % 2 == 0 && NSB >= 2, "copies per batch");
           auto copies = [&](int bi, bool is_v, int nb_batches) __attribute__((always_inline)) {
             if constexpr (kCopyBatched) {
               const int per = SEGW / nb_batches;
@@ -1611,7 +1622,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             }
 #pragma unroll
             for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
-            copies(bi, false, NSB);
+            if (bi < 2) {
+              copies(bi, false, 2);
+              copies(bi, true, 2);
+            }
             if (bi == 0) {
               __builtin_amdgcn_sched_barrier(0);
               // the partner's half of tile t's scores (same order in both
@@ -1669,11 +1683,18 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
               const int m = bi * KB + x, ks = m / NDB, db = m % NDB;
               oacc[db] = mfma32(as_bf16x8(vf[bi & 1][x]), as_bf16x8(pf[ks]), oacc[db]);
             }
-            copies(bi, true, NPV / KB);
           }
           __builtin_amdgcn_sched_barrier(0);
         } else {
           scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
+          if constexpr (kCopyInBlock) {
+            static_assert(NBUF == 2, "copies into the buffers the step frees");
+#pragma unroll
+            for (int x = 0; x < SEGW; ++x) {
+              prefill_seg(t_start + min(it + 2, n_tiles - 1) * BN, n_keys, kseq, false, kbuf(u), wave * SEGW + x);
+              prefill_seg(t_start + min(it + 1, n_tiles - 1) * BN, n_keys, vseq, true, vbuf(u ^ 1), wave * SEGW + x);
+            }
+          }
           u32x4 pf[NKS];
           exponentiate(sc, nb, pf);
           publish(sn, (it + 1) & 1);
@@ -1694,7 +1715,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           step(it + u, u);
         }
       }
-      if constexpr (D >= 512 && !KX) wait_vm<0>();   // the repeated copies after the last tile
+      if constexpr (kCopyBatched || kCopyInBlock) wait_vm<0>();   // the repeated copies after the last tile
 
     }
 
