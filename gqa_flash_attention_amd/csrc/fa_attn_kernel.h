@@ -1427,10 +1427,30 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       const int grp = wave >> 2;          // uniform
       f32x16 sc[NKB];
       u32x4 pf[NKS];
-      // this wave's two segments of one operand of the tile at key tb
-      auto copy2 = [&](int tb, const uint16_t* kv_base, bool is_v, uint16_t* dst) __attribute__((always_inline)) {
+      // this wave's two segments of one operand of the tile at key tb, as
+      // prefill_seg, with the per-lane parts of the source offsets (fixed
+      // for a wave) computed once: the softmax slot is the later one of the
+      // two, and each copy there then costs three VALU instructions instead
+      // of about seven
+      uint32_t kof[SEGW], vof[SEGW];
+      int crow[SEGW];
 #pragma unroll
-        for (int i = 0; i < SEGW; ++i) prefill_seg(tb, n_keys, kv_base, is_v, dst, wave * SEGW + i);
+      for (int i = 0; i < SEGW; ++i) {
+        const int sg = wave * SEGW + i;
+        kof[i] = p_lrk + 16u * (uint32_t)p_kchunk(sg);
+        vof[i] = p_lrv + 16u * (uint32_t)p_vchunk(sg);
+        crow[i] = sg * RPS + p_lr;
+      }
+      auto copy2 = [&](int tb, const uint16_t* kv_base, bool is_v, uint16_t* dst) __attribute__((always_inline)) {
+        const int lim = n_keys - 1 - tb;
+        const int rsb = ES * (is_v ? v_rs : k_rs);
+        const char* tbase = reinterpret_cast<const char*>(kv_base) + (int64_t)tb * rsb;
+#pragma unroll
+        for (int i = 0; i < SEGW; ++i) {
+          const int sg = wave * SEGW + i;
+          const uint32_t o = (is_v ? vof[i] : kof[i]) - (uint32_t)(max(crow[i] - lim, 0) * rsb);
+          dma16_buf_s<false>(tbase, o, (uint32_t)(sg * RPS * rsb), dst + sg * 512);
+        }
       };
       // softmax slot of tile t (ring position u = t % 3), at raised
       // priority: the issue arbiter then serves its VALU stream before the
