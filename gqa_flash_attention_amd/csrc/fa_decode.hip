@@ -67,6 +67,17 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
   const int h = (int)(t % c.Hq);
   const int b = (int)(t / c.Hq);
 
+  const float* lp = c.lse_part + row * c.n_slots;
+  const float* op = c.o_part + row * c.n_slots * D;
+  // The first block of LSEs is loaded before the row's slot count is known
+  // (every slot below n_slots lies in the buffer; those past the count are
+  // dropped below), so the two loads take one memory round trip.
+  float lv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k = lane + 64 * r;
+    lv[r] = k < c.n_slots ? lp[k] : -INFINITY;
+  }
   int n = c.n_slots;
   if (c.n_chunks != nullptr) {
     n = c.n_chunks[b];
@@ -76,9 +87,10 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
     n = len > 0 ? (int)(((int64_t)len + c.kv_chunk - 1) / c.kv_chunk) + 1 : 0;
   }
   n = max(0, min(n, c.n_slots));
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (lane + 64 * r >= n) lv[r] = -INFINITY;
 
-  const float* lp = c.lse_part + row * c.n_slots;
-  const float* op = c.o_part + row * c.n_slots * D;
   auto load_block = [&](int b0, float (&lv)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -86,8 +98,6 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs c) {
       lv[r] = k < n ? lp[k] : -INFINITY;
     }
   };
-  float lv[4];
-  load_block(0, lv);
   float m = fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3]));
   for (int b0 = 256; b0 < n; b0 += 256) {
     float lw[4];
