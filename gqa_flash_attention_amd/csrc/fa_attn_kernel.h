@@ -653,6 +653,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;   // reference max of the row (raw score units)
+  float nb_ref = 0.f;        // its exponent offset -m_run * sl2 (0 while m_run is -inf)
   float l_run = 0.f;         // this lane's part of the row sum
   // exponent factor: scores are raw q.k (scale folded in here), or with
   // score modifiers already scaled and modified (natural units)
@@ -791,15 +792,16 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       m_run = m_new;
+      nb_ref = m_run == -INFINITY ? 0.f : -m_run * sl2;
     }
-    return m_run == -INFINITY ? 0.f : -m_run * sl2;
+    return nb_ref;
   };
 
   // P = exp2(s*c - m*c) as bf16 pairs: already the B operand of O^T += V^T P^T.
   // The row sum adds the fp32 values: with few visible keys, summing the
   // bf16-rounded P would put bf16's 2^-9 relative error straight into LSE.
   auto exponentiate = [&](const f32x16 (&s)[NKB], float nb, u32x4 (&pf)[NKS]) {
-    float ls = 0.f;
+    float ls;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kb = ks >> 1, base = 8 * (ks & 1);
@@ -807,7 +809,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       for (int w = 0; w < 4; ++w) {
         const float e0 = fast_exp2(fmaf(s[kb][base + 2 * w], sl2, nb));
         const float e1 = fast_exp2(fmaf(s[kb][base + 2 * w + 1], sl2, nb));
-        ls += e0 + e1;
+        ls = (ks == 0 && w == 0) ? e0 + e1 : ls + (e0 + e1);
         pf[ks][w] = pack_bf16(e0, e1);
       }
     }
@@ -1040,6 +1042,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
       m_run = -INFINITY;
+      nb_ref = 0.f;
       l_run = 0.f;
     };
 
