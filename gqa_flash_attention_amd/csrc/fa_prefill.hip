@@ -8,13 +8,15 @@ namespace {
 
 // Tile shape per head dim: waves per workgroup, keys per tile, D split (two
 // waves per 32 rows) and the waves per SIMD the register budget is sized for.
-// Head dim 256 splits D so that a wave's registers fit two waves per SIMD
-// (measured on MI355X: 14% faster than one full-D wave per SIMD); head dim
-// 512 fills LDS with one workgroup per CU either way.
+// Head dim 256 runs one full-D wave per SIMD (Q fed to the MFMAs from AGPRs):
+// measured on MI355X 7 % faster than a D split over two waves per 32 rows
+// at two waves per SIMD, which exponentiated every tile twice and exchanged
+// partial scores through LDS. Head dim 512 keeps the split: one full-D
+// wave's O alone would fill the register file.
 template <int D> struct PrefillCfg;
 template <> struct PrefillCfg<64>  { static constexpr int NW = 4, BN = 64, DS = 1, WPE = 2; };
 template <> struct PrefillCfg<128> { static constexpr int NW = 4, BN = 64, DS = 1, WPE = 2; };
-template <> struct PrefillCfg<256> { static constexpr int NW = 8, BN = 32, DS = 2, WPE = 2; };
+template <> struct PrefillCfg<256> { static constexpr int NW = 4, BN = 32, DS = 1, WPE = 1; };
 template <> struct PrefillCfg<512> { static constexpr int NW = 4, BN = 32, DS = 2, WPE = 1; };
 
 template <int D>
