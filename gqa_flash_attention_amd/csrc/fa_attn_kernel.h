@@ -733,7 +733,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 
   // Mask the boundary tiles, update the reference max (lazily), and return
   // the exponent offset -m*c for the tile starting at key tb.
-  auto prepare = [&](f32x16 (&s)[NKB], int tb) -> float {
+  auto mask_scores = [&](f32x16 (&s)[NKB], int tb) {
     if constexpr (kXform) {
       // s -> softcap(scale * s) + slope * (key - p) + mask, before the
       // causal / window / length mask
@@ -774,6 +774,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           s[kb][x] = (rel <= hi_lim && rel >= lo_lim) ? s[kb][x] : -INFINITY;
         }
     }
+  };
+  auto update_ref = [&](const f32x16 (&s)[NKB]) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -796,11 +798,15 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
     return nb_ref;
   };
+  auto prepare = [&](f32x16 (&s)[NKB], int tb) -> float {
+    mask_scores(s, tb);
+    return update_ref(s);
+  };
 
   // P = exp2(s*c - m*c) as bf16 pairs: already the B operand of O^T += V^T P^T.
   // The row sum adds the fp32 values: with few visible keys, summing the
   // bf16-rounded P would put bf16's 2^-9 relative error straight into LSE.
-  auto exponentiate = [&](const f32x16 (&s)[NKB], float nb, u32x4 (&pf)[NKS]) {
+  auto exp_sum = [&](const f32x16 (&s)[NKB], float nb, u32x4 (&pf)[NKS]) -> float {
     float ls;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -813,6 +819,31 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         pf[ks][w] = pack_bf16(e0, e1);
       }
     }
+    return ls;
+  };
+  auto exponentiate = [&](const f32x16 (&s)[NKB], float nb, u32x4 (&pf)[NKS]) { l_run += exp_sum(s, nb, pf); };
+
+  // The softmax of one tile without the row max in the common case: once
+  // every row of the wave has a reference max, the tile is exponentiated
+  // against it first. Every weight is at most this lane's part of the row
+  // sum, so a part of at most 2^kRescaleLog2 (not NaN) means no weight
+  // exceeds the bound the lazy rescale keeps, and the tile needs neither the
+  // max nor a rescale. Otherwise (any lane of the wave; rare once the first
+  // tiles are done) the row max is taken, the reference updated as in
+  // prepare, and the tile exponentiated again. Saves the max reduction's
+  // VALU work (~20 of ~130 instructions per 64-key tile and lane) on most
+  // tiles; used by the ping-pong prefill, whose softmax slot is VALU work
+  // only (in the other kernels the extra live scores cost more registers
+  // than the saved instructions gain).
+  auto softmax_tile = [&](f32x16 (&s)[NKB], int tb, u32x4 (&pf)[NKS]) {
+    mask_scores(s, tb);
+    bool slow = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    float ls = 0.f;
+    if (!slow) {
+      ls = exp_sum(s, nb_ref, pf);
+      slow = __builtin_amdgcn_ballot_w64(!(ls <= kRescaleSum)) != 0;
+    }
+    if (slow) ls = exp_sum(s, update_ref(s), pf);
     l_run += ls;
   };
 
@@ -1462,8 +1493,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       auto vphase = [&](int t, int u) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         copy2(t_start + min(t + 2, n_tiles - 1) * BN, kseq, false, kbuf((u + 2) % 3));
-        const float nb = prepare(sc, t_start + t * BN);
-        exponentiate(sc, nb, pf);
+        softmax_tile(sc, t_start + t * BN, pf);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) pin_vgpr(pf[ks]);
         pin_vgpr(l_run);

@@ -85,6 +85,45 @@ def test_prefill_empty_kv_and_rows():
     assert o.numel() == 0
 
 
+# Scores that grow along the keys: a component shared by every query and by
+# the keys past `start`, growing with the key index, moves the row max by
+# many powers of two from tile to tile (every lazy-rescale path: the
+# reference max moves on most tiles after `start`, and a tile whose weights
+# pass the bound after being exponentiated against the old reference is
+# exponentiated again), and with `spike` a single late key dominates.
+GROW = [
+    # B, S, Hq, Hkv, D, causal, start, slope, spike
+    (1, 600, 8, 2, 128, 1, 200, 0.02, 0),
+    (1, 600, 8, 2, 128, 0, 300, 0.05, 0),
+    (1, 600, 8, 2, 128, 1, 0, 0.0, 451),
+    (1, 400, 4, 2, 64, 1, 100, 0.03, 0),
+    (1, 400, 4, 2, 256, 1, 100, 0.03, 333),
+    (1, 300, 4, 2, 512, 1, 50, 0.03, 0),
+]
+
+
+@pytest.mark.parametrize("case", GROW, ids=lambda c: "S{1}_H{2}x{3}_D{4}_c{5}_start{6}_sl{7}_spike{8}".format(*c))
+def test_prefill_growing_scores(case):
+    B, S, Hq, Hkv, D, causal, start, slope, spike = case
+    print(f"case {case}", flush=True)
+    q, k, v = workloads.random_inputs(B, S, S, Hq, Hkv, D, seed=17 + D + S)
+    gen = torch.Generator("cpu").manual_seed(99)
+    u = torch.randn(D, generator=gen) / np.sqrt(D)
+    qf, kf = q.float(), k.float()
+    qf = qf + 2.0 * u
+    ramp = torch.clamp(torch.arange(S, dtype=torch.float32) - start, min=0) * slope
+    kf = kf + (ramp[None, :, None, None] * np.sqrt(D)) * u
+    if spike:
+        kf[:, spike] = kf[:, spike] + 6.0 * np.sqrt(D) * u
+    q, k = qf.to(torch.bfloat16), kf.to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = _run(q, k, v, causal, 0, scale)
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, causal=bool(causal), scale=scale)
+    # the shared component spans many powers of two of the softmax weights
+    assert float(np.nanmax(lse_ref) - np.nanmin(lse_ref)) > 10.0
+    assert_parity(o, lse, o_ref, lse_ref, f"prefill growing scores {case}")
+
+
 def test_prefill_deterministic():
     q, k, v = workloads.random_inputs(2, 300, 300, 8, 2, 128, seed=5)
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)

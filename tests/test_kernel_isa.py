@@ -109,16 +109,25 @@ def test_prefill_main_block_keeps_copies_and_reads_in_flight(asm, kernel):
 
 
 def test_ping_pong_slots_stay_apart(asm):
-    blocks = [b for b in _blocks(_function(asm["prefill"], PREFILL_D128))
-              if sum(i.startswith("v_mfma") for i in b) >= 32 and sum(i.startswith("v_exp") for i in b) >= 32]
-    assert len(blocks) == 3, "one softmax + MFMA block per ring position expected"
-    for b in blocks:
-        bar = [k for k, i in enumerate(b) if i.startswith("s_barrier")]
-        exps = [k for k, i in enumerate(b) if i.startswith("v_exp")]
-        mfma = [k for k, i in enumerate(b) if i.startswith("v_mfma")]
-        assert len(bar) >= 1, "no slot barrier inside the block"
-        assert max(exps) < bar[0] < min(mfma), "softmax and MFMA work mixed across the slot barrier"
-        assert all(max(mfma) < k for k in bar[1:]), "MFMA work after the MFMA slot's closing barrier"
+    """In the ping-pong loop every stretch between two workgroup barriers is
+    one slot: softmax work (exponentials, on the fast path or its rare
+    fallback) or MFMA work, never both; one of each per ring position."""
+    loop = [l.strip() for l in _loop(_function(asm["prefill"], PREFILL_D128))
+            if l.startswith("\t") and not l.strip().startswith((";", "."))]
+    segs, cur = [], []
+    for ins in loop:
+        if ins.startswith("s_barrier"):
+            segs.append(cur)
+            cur = []
+        else:
+            cur.append(ins)
+    # the loop may be laid out rotated: its last stretch continues its first
+    segs[0] = cur + segs[0]
+    n_exp = [sum(i.startswith("v_exp") for i in g) for g in segs]
+    n_mfma = [sum(i.startswith("v_mfma") for i in g) for g in segs]
+    assert not any(e and m for e, m in zip(n_exp, n_mfma)), "softmax and MFMA work mixed inside one slot"
+    assert sum(m >= 32 for m in n_mfma) == 3, "one MFMA slot (32 MFMAs) per ring position expected"
+    assert sum(e >= 32 for e in n_exp) == 3, "one softmax slot (32 exponentials) per ring position expected"
 
 
 def test_split_loop_reads_tiles_without_full_drain(asm):
