@@ -239,6 +239,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // (the main loop below); head dim 128 without score modifiers.
   constexpr bool PP = !SPLIT && DS == 1 && NW == 8;
   static_assert(!PP || (NBUF == 3 && BN == 64 && !KV8 && !KX && (MODS == 0 || MODS == 1)), "ping-pong prefill");
+  // Prefill at head dim 256 holds one workgroup per CU, so nothing covers a
+  // block of rows' start (its Q from HBM, the first tiles) and end (O out):
+  // measured on MI355X ~12 us per block against ~0.9 us per 32-key tile.
+  // This kernel runs a persistent grid instead: each workgroup takes several
+  // blocks of rows in turn and loads the next block's Q fragments and first
+  // tiles before writing the current block's O. (At head dim 512 the same
+  // loop spills registers.)
+  constexpr bool PERS = !SPLIT && !PP && D == 256 && !KX;
   // MODS level: 0 plain, 1 score transform (softcap, ALiBi), 2 transform +
   // mask, 3 plain with head dims below D, 4 transform + mask + head dims
   // below D
@@ -299,6 +307,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   }
   // partial scores exchanged by the waves of a D split, [slot][wave][value][lane]
   __shared__ float sX[DS > 1 ? XSLOTS : 1][DS > 1 ? NW : 1][DS > 1 ? NKB * 16 : 1][64];
+  // O staging of the persistent prefill at head dims up to 256 (the tile
+  // buffers then already hold the next block's first tiles)
+  __shared__ __attribute__((aligned(1024))) uint16_t sO[(PERS && D <= 256) ? BM * D : 8];
   // extra key columns (KX), one buffer per K tile buffer
   __shared__ __attribute__((aligned(1024))) uint16_t sKx0[KX ? BN * DXK : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t sKx1[KX ? BN * DXK : 8];
@@ -567,7 +578,28 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   int ke = 0;                  // end (exclusive) of the keys the current tile may hold
   bf16x8 qf[NQC];
   bf16x8 qfx[NQX];     // KX: this wave's share of the 64 extra query columns
-  auto set_rows = [&](int b_, int g_, int rb_, int n_keys) {
+  // This lane's Q fragments of row block rb_ of (sequence b_, KV head g_),
+  // as set_rows loads them (the persistent prefill's prefetch of the next
+  // block)
+  auto load_q = [&](int b_, int g_, int rb_) {
+    const int rows = a.Sq * a.G;
+    const int r_lo = rb_ * BM;
+    const int r_hi = min(r_lo + BM, rows);
+    const int r = r_lo + 32 * rg + j;
+    const bool ok = r < r_hi;
+    const int qi_ = ok ? r / a.G : 0;
+    const int qh_ = g_ * a.G + (ok ? r % a.G : 0);
+    const int64_t qoff = (int64_t)b_ * a.q_sb + (int64_t)qi_ * a.q_ss + (int64_t)qh_ * a.q_sh +
+                         8 * hl + dh * (D / DS);
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      const bool in_d = !kPad || 8 * hl + dh * (D / DS) + 16 * c < a.dk;
+      if (ok && in_d) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
+      qf[c] = as_bf16x8(w);
+    }
+  };
+  auto set_rows = [&](int b_, int g_, int rb_, int n_keys, bool with_q = true) {
     b = b_;
     const int rows = a.Sq * a.G;
     const int r_lo = rb_ * BM;
@@ -594,12 +626,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
     const int64_t qoff = (int64_t)b_ * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)qh * a.q_sh +
                          8 * hl + dh * (D / DS);
+    if (with_q) {
 #pragma unroll
-    for (int c = 0; c < NQC; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      const bool in_d = !kPad || 8 * hl + dh * (D / DS) + 16 * c < a.dk;
-      if (row_ok && in_d) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
-      qf[c] = as_bf16x8(w);
+      for (int c = 0; c < NQC; ++c) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        const bool in_d = !kPad || 8 * hl + dh * (D / DS) + 16 * c < a.dk;
+        if (row_ok && in_d) w = *reinterpret_cast<const u32x4*>(a.q + qoff + 16 * c);
+        qf[c] = as_bf16x8(w);
+      }
     }
     if constexpr (KX) {
       // columns D + 16 (dh NQX + c) + 8 hl .. + 7
@@ -1395,34 +1429,68 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       }
     }
   } else {
-    // ======================= prefill: one block of rows per workgroup ==========
+    // ======================= prefill: blocks of rows ==========================
+    // One block of rows per workgroup, or (PERS) a persistent grid: the
+    // workgroups on XCD x (workgroup w runs on XCD w % 8) take, in zig-zag
+    // rounds, the blocks a one-block-per-workgroup grid would give that XCD
+    // (xcd_remap), heaviest first within each (b, KV head). Consecutive
+    // rounds pair heavy with light blocks, so the workgroups of an XCD get
+    // nearly equal work, and the blocks sharing K/V share an L2.
     const int n = a.B * a.Hkv * a.n_rb;
-    const int L = xcd_remap(blockIdx.x, n);
+    const int n_keys = a.skv;
+    ke = n_keys;
+    const int rows = a.Sq * a.G;
+    const int shift = n_keys - a.Sq;
+    auto pers_item = [&](int r) -> int {
+      constexpr int X = 8;
+      const int G = gridDim.x, w = blockIdx.x;
+      const int x = w % X, k = w / X;
+      const int P = G / X + (x < G % X ? 1 : 0);
+      const int per = n / X, rem = n % X;
+      const int cnt = per + (x < rem ? 1 : 0);
+      const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+      const int jl = r * P + ((r & 1) ? P - 1 - k : k);
+      return jl < cnt ? base + jl : -1;
+    };
+    // the whole tiles holding the keys block rb_ may attend to
+    auto block_tiles = [&](int rb_, int& t_start_, int& n_tiles_) {
+      const int r_lo_ = rb_ * BM, r_hi_ = min(r_lo_ + BM, rows);
+      const int pmin = r_lo_ / a.G + shift, pmax = (r_hi_ - 1) / a.G + shift;
+      int kv_lo = 0, kv_hi = n_keys;
+      if (a.causal) {
+        kv_hi = min(kv_hi, pmax + 1);
+        if (a.window > 0) kv_lo = max(kv_lo, pmin - a.window + 1);
+      }
+      t_start_ = (max(kv_lo, 0) / BN) * BN;
+      n_tiles_ = kv_hi > kv_lo ? (kv_hi - t_start_ + BN - 1) / BN : 0;
+    };
+    int L = PERS ? pers_item(0) : xcd_remap(blockIdx.x, n);
+    bool pre = false;    // PERS: this block's Q fragments and first tiles are already loading
+    for (int round = 0; L >= 0; ++round) {
     const int bg = L / a.n_rb;
     const int rb = a.n_rb - 1 - (L % a.n_rb);   // heaviest causal row blocks first
     const int bq = bg / a.Hkv;
     const int g = bg % a.Hkv;
-    const int n_keys = a.skv;
-    ke = n_keys;
-    const int rows = a.Sq * a.G;
     const int r_lo = rb * BM;
     const int r_hi = min(r_lo + BM, rows);
-    const int shift = n_keys - a.Sq;
-    const int pmin = r_lo / a.G + shift;
-    const int pmax = (r_hi - 1) / a.G + shift;
-    int kv_lo = 0, kv_hi = n_keys;
-    if (a.causal) {
-      kv_hi = min(kv_hi, pmax + 1);
-      if (a.window > 0) kv_lo = max(kv_lo, pmin - a.window + 1);
+    int t_start = 0, n_tiles = 0;
+    block_tiles(rb, t_start, n_tiles);
+    set_rows(bq, g, rb, n_keys, !pre);
+    if constexpr (PERS) {
+      if (round > 0) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+        m_run = -INFINITY;
+        nb_ref = 0.f;
+        l_run = 0.f;
+      }
     }
-    const int t_start = (max(kv_lo, 0) / BN) * BN;
-    const int n_tiles = kv_hi > kv_lo ? (kv_hi - t_start + BN - 1) / BN : 0;
-    set_rows(bq, g, rb, n_keys);
     const uint16_t* kseq;
     const uint16_t* vseq;
     kv_bases(bq, g, kseq, vseq);
     auto issue_k = [&](int tb, uint16_t* dst) { issue(tb, n_keys, kseq, bq, false, dst); };
     auto issue_v = [&](int tb, uint16_t* dst) { issue(tb, n_keys, vseq, bq, true, dst); };
+    int L_next = -1;
 
     if constexpr (PP) {
       // ---- main loop, two wave groups in ping-pong -----------------------------
@@ -1583,14 +1651,20 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       constexpr int LATER_STEP = (NBUF - 2) * GROUP < 63 ? (NBUF - 2) * GROUP : 63;
       constexpr int LATER_PRO = (NBUF - 1) * GROUP < 63 ? (NBUF - 1) * GROUP : 63;
       f32x16 sc[NKB];
-      if (n_tiles > 0) {
-        issue_k(t_start, kbuf(0));
+      // the first tiles: K(0 .. NBUF-1), V(0 .. NBUF-2) of the block starting at key ts_
+      auto issue_first = [&](int ts_, int nt_, const uint16_t* kb_, const uint16_t* vb_, int b_) {
+        issue(ts_, n_keys, kb_, b_, false, kbuf(0));
 #pragma unroll
         for (int jj = 0; jj < NBUF - 1; ++jj) {
-          if (jj + 1 < n_tiles) issue_k(t_start + (jj + 1) * BN, kbuf(jj + 1));
-          if (jj < n_tiles) issue_v(t_start + jj * BN, vbuf(jj));
+          if (jj + 1 < nt_) issue(ts_ + (jj + 1) * BN, n_keys, kb_, b_, false, kbuf(jj + 1));
+          if (jj < nt_) issue(ts_ + jj * BN, n_keys, vb_, b_, true, vbuf(jj));
         }
-        if (NBUF - 1 < n_tiles) wait_vm<LATER_PRO>(); else wait_vm<0>();
+      };
+      if (n_tiles > 0) {
+        if (!pre) issue_first(t_start, n_tiles, kseq, vseq, bq);
+        // (a block whose first tiles were issued during the previous block's
+        // end waits for everything: that block's O stores followed them)
+        if (pre || NBUF - 1 >= n_tiles) wait_vm<0>(); else wait_vm<LATER_PRO>();
         lds_barrier();
         scores(kbuf(0), sc);
         publish(sc, 0);
@@ -1771,6 +1845,27 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         }
       }
       if constexpr (kCopyBatched || kCopyInBlock) wait_vm<0>();   // the repeated copies after the last tile
+      if constexpr (PERS) {
+        static_assert(kCopyBatched || kCopyInBlock, "the loop leaves no copy in flight");
+        // the next block: its Q fragments (qf is free once the last scores
+        // are done) and, once every wave is past the last tiles, its first
+        // tiles, all in flight while this block's O goes out
+        L_next = pers_item(round + 1);
+        pre = false;
+        if (L_next >= 0) {
+          const int bg2 = L_next / a.n_rb, rb2 = a.n_rb - 1 - (L_next % a.n_rb);
+          const int bq2 = bg2 / a.Hkv, g2 = bg2 % a.Hkv;
+          int ts2 = 0, nt2 = 0;
+          block_tiles(rb2, ts2, nt2);
+          load_q(bq2, g2, rb2);
+          lds_barrier();
+          const uint16_t* k2;
+          const uint16_t* v2;
+          kv_bases(bq2, g2, k2, v2);
+          if (nt2 > 0) issue_first(ts2, nt2, k2, v2, bq2);
+          pre = true;
+        }
+      }
 
     }
 
@@ -1780,7 +1875,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     // barriers (measured 7 % slower), and a lane's fragments go straight out.
     constexpr bool kStageO = D <= 256;
     const float l_tot = pair_sum(l_run);
-    if constexpr (!kStageO) {
+    if constexpr (!kStageO && !PERS) {
       if (!row_ok) return;
     }
     const bool empty = !(l_tot > 0.f);
@@ -1800,6 +1895,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     }
     if constexpr (!kStageO) {
       uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)qh * a.o_sh;
+      if (row_ok)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1820,6 +1916,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       constexpr int CH = D / 8;                 // 16-byte chunks per row
       static_assert(BM <= 4 * BN && NBUF >= 2, "the staged block fits four tile buffers");
       auto stage = [&](int row) -> uint16_t* {
+        if constexpr (PERS) return sO + row * D;
         const int r = row % BN;
         uint16_t* base = row < BN ? sK0 : row < 2 * BN ? sK1 : row < 3 * BN ? sV0 : sV1;
         return base + r * D;
@@ -1852,9 +1949,14 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
                                     8 * c) = v;
         }
       }
-      if (!row_ok) return;
+      if constexpr (!PERS) {
+        if (!row_ok) return;
+      }
     }
-    if (a.lse != nullptr && hl == 0 && dh == 0) a.lse[((int64_t)b * a.Hq + qh) * a.Sq + qi] = lse_v;
+    if (a.lse != nullptr && hl == 0 && dh == 0 && row_ok) a.lse[((int64_t)b * a.Hq + qh) * a.Sq + qi] = lse_v;
+    if constexpr (!PERS) break;
+    L = L_next;
+    }  // rounds of the persistent grid
   }
 }
 

@@ -75,21 +75,22 @@ hipError_t run(const PrefillDesc& d, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  if (level == 4)
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 4>), dim3((unsigned)grid),
-                       dim3(C::NW * 64), 0, stream, a);
-  else if (level == 3)
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 3>), dim3((unsigned)grid),
-                       dim3(C::NW * 64), 0, stream, a);
-  else if (level == 2)
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 2>), dim3((unsigned)grid),
-                       dim3(C::NW * 64), 0, stream, a);
-  else if (level == 1)
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 1>), dim3((unsigned)grid),
-                       dim3(C::NW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 0>), dim3((unsigned)grid),
-                       dim3(C::NW * 64), 0, stream, a);
+  using K = decltype(&attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 0>);
+  static const K kernels[5] = {
+      &attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 0>,
+      &attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 1>,
+      &attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 2>,
+      &attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 3>,
+      &attn_kernel<D, C::NW, C::BN, C::DS, 2, false, false, C::WPE, 4>};
+  const K kern = kernels[level];
+  int64_t g_launch = grid;
+  if constexpr (D == 256) {
+    // persistent kernels: as many workgroups as the GPU holds at once, each
+    // taking several blocks of rows
+    static std::atomic<int> cache[5][kResidentDevs];
+    g_launch = std::min<int64_t>(grid, resident_workgroups(kern, C::NW * 64, cache[level], stream));
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)g_launch), dim3(C::NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

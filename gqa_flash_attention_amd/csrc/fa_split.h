@@ -49,35 +49,6 @@ template <int D, int NWR> struct SplitCfg {
   static constexpr int WPE8_MASK = D == 128 ? WPE_MASK : 2;
 };
 
-// Workgroups of a kernel the GPU holds at once: CUs x resident workgroups per
-// CU. Measured on MI355X, a CU holds at most 144 KiB of LDS across
-// workgroups of 32 KiB or less (the occupancy query allows 160), so the
-// count is the smaller of the two. The device is the stream's (the current
-// one for the null stream). The answer is kept per device (the library's
-// only process state besides the no-allocation scratch array: a pure
-// function of the kernel and the device); devices past the table are
-// queried on every call.
-constexpr int kResidentDevs = 64;
-template <typename Kernel>
-int resident_workgroups(Kernel kernel, int threads, std::atomic<int>* cache, hipStream_t stream) {
-  int dev = 0;
-  const bool known = (stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) == hipSuccess;
-  const bool keep = known && dev >= 0 && dev < kResidentDevs;
-  if (keep) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int occ = 0, cus = 0;
-  hipFuncAttributes attr{};
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess) occ = 1;
-  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) == hipSuccess &&
-      attr.sharedSizeBytes > 0)
-    occ = std::min<int>(occ, (int)(147456 / attr.sharedSizeBytes));
-  if (!known || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
-  const int n = std::max(occ, 1) * std::max(cus, 1);
-  if (keep) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 template <int D, int NWR>
 hipError_t run_split(const SplitDesc& d, hipStream_t stream) {

@@ -154,6 +154,47 @@ def _rows(S):
     return np.unique(np.array(base + list(gen.integers(0, S, 17)))).astype(np.int64)
 
 
+# Head dim 256 runs a persistent grid (one workgroup per CU, each taking
+# several blocks of 128 rows in zig-zag rounds and loading the next block's
+# Q and first tiles before writing the current block's O). Shapes with more
+# blocks than workgroups exercise the rounds: rows sampled in every block,
+# blocks without any visible key (Sq > Skv) between ones with keys, and a
+# score transform.
+PERSISTENT = [
+    # B, Sq, Skv, Hq, Hkv, causal, window, softcap
+    (4, 2048, 2048, 16, 8, 1, 300, 0.0),
+    (8, 2048, 512, 8, 8, 1, 0, 0.0),
+    (2, 1536, 1536, 12, 4, 0, 0, 0.0),
+    (4, 2048, 2048, 16, 8, 1, 0, 20.0),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "B{}_Sq{}_Skv{}_H{}x{}_c{}_w{}_cap{}".format(*c))
+def test_prefill_persistent_rounds(case):
+    B, Sq, Skv, Hq, Hkv, causal, window, softcap = case
+    print(f"case {case}", flush=True)
+    D = 256
+    q, k, v = workloads.random_inputs(B, Sq, Skv, Hq, Hkv, D, seed=B * Sq + Skv + Hq)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=bool(causal), window=window, scale=scale,
+                        softcap=softcap)
+    torch.cuda.synchronize()
+    o, lse = to_np(o), to_np(lse)
+    G = Hq // Hkv
+    pos_per_block = 128 // G
+    gen = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(0, Sq, pos_per_block),
+                                     np.arange(pos_per_block - 1, Sq, pos_per_block),
+                                     gen.integers(0, Sq, 64)])).astype(np.int64)
+    heads = sorted({0, 1, Hq // 2, Hq - 1})
+    for b in sorted({0, B - 1}):
+        o_ref, lse_ref = oracle.attention_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=bool(causal),
+                                              window=window, scale=scale, rows=rows, heads=heads,
+                                              softcap=softcap)
+        assert_parity(o[b:b + 1][:, rows][:, :, heads], lse[b:b + 1][:, heads][:, :, rows],
+                      o_ref[:, rows][:, :, heads], lse_ref[:, heads][:, :, rows], f"persistent {case} b{b}")
+
+
 def test_prefill_c2_full_size_sampled():
     s = workloads.C2
     q, k, v = workloads.prefill_inputs(s)
