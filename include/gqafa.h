@@ -15,10 +15,10 @@
  *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned, owned by the
  *     caller. The library never allocates, frees or synchronizes. Its only
  *     process state is a per-(kernel, device) count of the workgroups a
- *     device holds at once (the split-KV kernels' grid size), computed on a
- *     device's first decode call from the runtime's occupancy query; it is a
- *     pure function of the kernel and the device, so no result depends on
- *     call history.
+ *     device holds at once (the grid size of the split-KV kernels and of the
+ *     persistent head-dim-256 prefill), computed on a kernel's first call on
+ *     a device from the runtime's occupancy query; it is a pure function of
+ *     the kernel and the device, so no result depends on call history.
  *   - bf16 tensors are passed as raw 16-bit storage (bfloat16 bit patterns).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     default stream). Results are ready when the stream reaches the call.
