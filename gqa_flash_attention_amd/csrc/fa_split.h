@@ -47,6 +47,12 @@ template <int D, int NWR> struct SplitCfg {
   // workgroups per CU at 256, one at 512 by LDS).
   static constexpr int WPE8 = 2;
   static constexpr int WPE8_MASK = D == 128 ? WPE_MASK : 2;
+  // keys per fp8 tile: the one-wave head-dim-128 kernel takes 64 (the bytes
+  // of a 32-key bf16 tile) at one wave per SIMD, so it runs the bf16
+  // kernel's step count per byte
+  static constexpr int BN8 = (D == 128 && NW == 1) ? 64 : 32;
+  static constexpr int WPE8_1 = (D == 128 && NW == 1) ? 1 : WPE8;
+  static constexpr int WPE8M_1 = (D == 128 && NW == 1) ? 1 : WPE8_MASK;
 };
 
 
@@ -124,10 +130,10 @@ hipError_t run_split(const SplitDesc& d, hipStream_t stream) {
       // fp8 caches: plain, or score transform and mask (softcap / ALiBi alone
       // run with a null mask)
       static const K kernels8[2][2] = {
-          {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE8, 0, true>,
-           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8, false, true, C::WPE8_MASK, 2, true>},
-          {attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE8, 0, true>,
-           attn_kernel<D, NW, C::BN, C::DS, C::NBUF8P, true, true, C::WPE8_MASK, 2, true>}};
+          {attn_kernel<D, NW, C::BN8, C::DS, C::NBUF8, false, true, C::WPE8_1, 0, true>,
+           attn_kernel<D, NW, C::BN8, C::DS, C::NBUF8, false, true, C::WPE8M_1, 2, true>},
+          {attn_kernel<D, NW, C::BN8, C::DS, C::NBUF8P, true, true, C::WPE8_1, 0, true>,
+           attn_kernel<D, NW, C::BN8, C::DS, C::NBUF8P, true, true, C::WPE8M_1, 2, true>}};
       static std::atomic<int> cache8[2][2][kResidentDevs];
       const int l8 = level == 0 ? 0 : 1;
       k = kernels8[paged][l8];

@@ -35,6 +35,50 @@ def _deq(codes, scale):
     return oracle.dequantize_e4m3(codes.numpy(), scale.numpy())
 
 
+@pytest.mark.parametrize("D", [128, 256, 512])
+def test_fp8_every_code_widens_exactly(D):
+    """Every finite e4m3 code through the kernels' widening, both paths: one
+    key per sequence, so O is that key's V row (each code once per 128
+    columns) and LSE is its single score; with one-hot queries the score is
+    one K element times the softmax scale (unit dequantisation scales)."""
+    print(f"fp8 codes D={D}", flush=True)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)   # 254 finite codes
+    B, Hq, Hkv = 2 * (D // 32), 32, 1
+    # sequence b holds 128 codes (half b % 2 of the code list) in V at columns
+    # (c + 37 b) % D, and in K; query head h of sequence b is one-hot at
+    # column d = 32 (b // 2) + h
+    half = [codes[:128], np.concatenate([codes[128:], codes[:2]])]
+    kc = np.zeros((B, 1, Hkv, D), np.uint8)
+    vc = np.zeros((B, 1, Hkv, D), np.uint8)
+    for b in range(B):
+        row = np.resize(half[b % 2], D)
+        kc[b, 0, 0] = row
+        vc[b, 0, 0] = np.roll(row, 37 * b)
+    q = torch.zeros((B, 1, Hq, D), dtype=torch.bfloat16)
+    for b in range(B):
+        for h in range(Hq):
+            q[b, 0, h, 32 * (b // 2) + h] = 1.0
+    one = torch.ones(Hkv, dtype=torch.float32)
+    lens = torch.ones(B, dtype=torch.int32)
+    scale = 0.125
+    o, lse = fa.decode_paged_fp8(q.to(DEV), torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV),
+                                 one.to(DEV), one.to(DEV), None, lens.to(DEV), page_size=1, kv_chunk=32,
+                                 scale=scale)
+    torch.cuda.synchronize()
+    vref = oracle.dequantize_e4m3(vc, one.numpy())            # fp64 [B, 1, 1, D]
+    kref = oracle.dequantize_e4m3(kc, one.numpy())
+    o = to_np(o)
+    lse = to_np(lse)
+    for b in range(B):
+        np.testing.assert_array_equal(o[b, 0], np.broadcast_to(vref[b, 0, 0], (Hq, D)))
+        d = 32 * (b // 2) + np.arange(Hq)
+        np.testing.assert_allclose(lse[b, :, 0], kref[b, 0, 0, d] * scale, rtol=1e-6, atol=1e-30)
+    # the one-hot queries read every finite code out of K, and every V row holds its half of them
+    seen_k = {int(x) for b in range(B) for x in kc[b, 0, 0][32 * (b // 2):32 * (b // 2) + 32]}
+    seen_v = {int(x) for b in range(B) for x in vc[b, 0, 0]}
+    assert seen_k == set(codes.tolist()) and seen_v == set(codes.tolist())
+
+
 @pytest.mark.parametrize("paged", [True, False])
 def test_fp8_append_bitexact(paged):
     print(f"fp8 append paged={paged}", flush=True)
