@@ -1444,6 +1444,12 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     auto pers_item = [&](int r) -> int {
       constexpr int X = 8;
       const int G = gridDim.x, w = blockIdx.x;
+      // fewer workgroups than XCDs (a small grid): some XCD would have no
+      // workgroup for its chunk, so the blocks are dealt round-robin instead
+      if (G < X) {
+        const int64_t Lr = (int64_t)r * G + w;
+        return Lr < n ? (int)Lr : -1;
+      }
       const int x = w % X, k = w / X;
       const int P = G / X + (x < G % X ? 1 : 0);
       const int per = n / X, rem = n % X;
