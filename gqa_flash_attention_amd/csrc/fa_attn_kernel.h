@@ -245,7 +245,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
   // This kernel runs a persistent grid instead: each workgroup takes several
   // blocks of rows in turn and loads the next block's Q fragments and first
   // tiles before writing the current block's O. (At head dim 512 the same
-  // loop spills registers.)
+  // loop, with its copy lambdas forced inline so that it does not spill,
+  // measured 1 % slower: 2048 causal blocks of one wave per SIMD balance
+  // better under the hardware's own dispatch.)
   constexpr bool PERS = !SPLIT && !PP && D == 256 && !KX;
   // MODS level: 0 plain, 1 score transform (softcap, ALiBi), 2 transform +
   // mask, 3 plain with head dims below D, 4 transform + mask + head dims
