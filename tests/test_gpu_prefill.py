@@ -161,23 +161,32 @@ def _rows(S):
 # blocks without any visible key (Sq > Skv) between ones with keys, and a
 # score transform.
 PERSISTENT = [
-    # B, Sq, Skv, Hq, Hkv, causal, window, softcap
-    (4, 2048, 2048, 16, 8, 1, 300, 0.0),
-    (8, 2048, 512, 8, 8, 1, 0, 0.0),
-    (2, 1536, 1536, 12, 4, 0, 0, 0.0),
-    (4, 2048, 2048, 16, 8, 1, 0, 20.0),
+    # B, Sq, Skv, Hq, Hkv, causal, window, softcap, additive mask
+    (4, 2048, 2048, 16, 8, 1, 300, 0.0, False),
+    (8, 2048, 512, 8, 8, 1, 0, 0.0, False),
+    (2, 1536, 1536, 12, 4, 0, 0, 0.0, False),
+    (4, 2048, 2048, 16, 8, 1, 0, 20.0, False),
+    (4, 2048, 2048, 16, 8, 1, 0, 0.0, True),
 ]
 
 
-@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "B{}_Sq{}_Skv{}_H{}x{}_c{}_w{}_cap{}".format(*c))
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "B{}_Sq{}_Skv{}_H{}x{}_c{}_w{}_cap{}_mask{}".format(*c))
 def test_prefill_persistent_rounds(case):
-    B, Sq, Skv, Hq, Hkv, causal, window, softcap = case
+    B, Sq, Skv, Hq, Hkv, causal, window, softcap, with_mask = case
     print(f"case {case}", flush=True)
     D = 256
     q, k, v = workloads.random_inputs(B, Sq, Skv, Hq, Hkv, D, seed=B * Sq + Skv + Hq)
     scale = 1.0 / np.sqrt(D)
+    mask = None
+    if with_mask:
+        # N(0, 2) per (sequence, row, key), a hidden band of keys per sequence
+        g = torch.Generator().manual_seed(11)
+        m = 2.0 * torch.randn(B, Sq, Skv, generator=g)
+        for b in range(B):
+            m[b, :, 300 * b + 100:300 * b + 140] = -float("inf")
+        mask = m.to(torch.bfloat16)
     o, lse = fa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=bool(causal), window=window, scale=scale,
-                        softcap=softcap)
+                        softcap=softcap, mask=None if mask is None else mask.to(DEV))
     torch.cuda.synchronize()
     o, lse = to_np(o), to_np(lse)
     G = Hq // Hkv
@@ -190,7 +199,7 @@ def test_prefill_persistent_rounds(case):
     for b in sorted({0, B - 1}):
         o_ref, lse_ref = oracle.attention_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=bool(causal),
                                               window=window, scale=scale, rows=rows, heads=heads,
-                                              softcap=softcap)
+                                              softcap=softcap, mask=None if mask is None else mask[b:b + 1])
         assert_parity(o[b:b + 1][:, rows][:, :, heads], lse[b:b + 1][:, heads][:, :, rows],
                       o_ref[:, rows][:, :, heads], lse_ref[:, heads][:, :, rows], f"persistent {case} b{b}")
 
