@@ -1583,9 +1583,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
         copy2(t_start + min(t + 2, n_tiles - 1) * BN, vseq, true, vbuf((u + 2) % 3));
         accumulate(vbuf(u), pf);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        sched_phase_copies<NKB * NQC, 1, 4, 3, 9, 0>();
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        sched_phase<NDB * NKS, 2, 4, 0, 0>();
+        sched_cont<NKB * NQC, 1, NDB * NKS, 2, 4, 0, 3, 9, 0>();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) pin_vgpr(sc[kb]);
 #pragma unroll
@@ -1743,6 +1741,17 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             }
           };
           u32x4 kf[2][KB];
+          constexpr int NPV = NKS * NDB;
+          auto vread = [&](int m, u32x4& out) {
+            const int ks = m / NDB, db = m % NDB;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
+              out[2 * half] = t[0];
+              out[2 * half + 1] = t[1];
+            }
+          };
+          u32x4 vf[2][KB];
 #pragma unroll
           for (int x = 0; x < KB; ++x) kf[0][x] = kread(x);
           sn[0] = f32x16{};
@@ -1754,6 +1763,11 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
             if (bi + 1 < NSB) {
 #pragma unroll
               for (int x = 0; x < KB; ++x) kf[(bi + 1) & 1][x] = kread((bi + 1) * KB + x);
+            } else {
+              // the first PV batch's V^T reads beside the last score batch
+              // (V(t) landed before this step's barrier)
+#pragma unroll
+              for (int x = 0; x < KB; ++x) vread(x, vf[0][x]);
             }
 #pragma unroll
             for (int x = 0; x < KB; ++x) sn[0] = mfma32(as_bf16x8(kf[bi & 1][x]), qf[bi * KB + x], sn[0]);
@@ -1793,19 +1807,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           }
           publish(sn, (it + 1) & 1);
           // O^T += V^T P^T in batches of KB MFMAs, two transposing reads each
-          constexpr int NPV = NKS * NDB;
-          auto vread = [&](int m, u32x4& out) {
-            const int ks = m / NDB, db = m % NDB;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const u32x2 t = read_tr16(&bv[v_elem(ks, half, db)]);
-              out[2 * half] = t[0];
-              out[2 * half + 1] = t[1];
-            }
-          };
-          u32x4 vf[2][KB];
-#pragma unroll
-          for (int x = 0; x < KB; ++x) vread(x, vf[0][x]);
+          // (the first batch's reads went out with the last score batch)
 #pragma unroll
           for (int bi = 0; bi < NPV / KB; ++bi) {
             __builtin_amdgcn_sched_barrier(0);
@@ -1839,7 +1841,13 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           // MFMAs each followed by the next two V^T reads; reads run 4 ahead
           // of their MFMAs, 6 at head dim 256 (one wave per SIMD, nothing
           // else covers its LDS latency: measured 2 % faster; 8: no gain)
-          sched_step<NKB * NQC, 1, NDB * NKS, 2, (D == 256 ? 6 : 4), kExpValuPerTile / (NKB * NQC)>();
+          {
+            // the operand reads as one stream over both phases (the PV
+            // phase's first reads beside the last score MFMAs)
+            constexpr int kAh = D == 256 ? 6 : 4;
+            __builtin_amdgcn_sched_group_barrier(0x100, kAh, 0);
+            sched_cont<NKB * NQC, 1, NDB * NKS, 2, kAh, kExpValuPerTile / (NKB * NQC), -1, -1, 0>();
+          }
         }
         if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
 #pragma unroll

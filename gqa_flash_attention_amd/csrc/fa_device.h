@@ -143,6 +143,28 @@ __device__ __forceinline__ void sched_phase_copies() {
     sched_phase_copies<N, R, AHEAD, C1, C2, I + 1>();
   }
 }
+// One continuous operand-read stream over both phases of a step: N1 MFMAs
+// that consume R1 LDS reads each (hiding V1 VALU instructions each), then
+// N2 MFMAs consuming R2 reads each, with the reads AHEAD in front of their
+// MFMAs across the phase boundary (the second phase's first reads go out
+// beside the first phase's last MFMAs instead of after them), and one
+// vector memory instruction after MFMAs C1 and C2. The caller issues the
+// first AHEAD reads.
+template <int N1, int R1, int N2, int R2, int AHEAD, int V1, int C1, int C2, int I>
+__device__ __forceinline__ void sched_cont() {
+  if constexpr (I < N1 + N2) {
+    constexpr int total = N1 * R1 + N2 * R2;
+    constexpr int used = I < N1 ? (I + 1) * R1 : N1 * R1 + (I + 1 - N1) * R2;
+    constexpr int used_prev = I == 0 ? 0 : (I - 1 < N1 ? I * R1 : N1 * R1 + (I - N1) * R2);
+    constexpr int lo = used_prev + AHEAD < total ? used_prev + AHEAD : total;
+    constexpr int hi = used + AHEAD < total ? used + AHEAD : total;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);
+    if constexpr (I < N1 && V1 > 0) __builtin_amdgcn_sched_group_barrier(0x002, V1, 0);
+    if constexpr (I == C1 || I == C2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    sched_cont<N1, R1, N2, R2, AHEAD, V1, C1, C2, I + 1>();
+  }
+}
 template <int N1, int R1, int N2, int R2, int AHEAD, int V1>
 __device__ __forceinline__ void sched_step() {
   constexpr int a1 = AHEAD < N1 * R1 ? AHEAD : N1 * R1;
