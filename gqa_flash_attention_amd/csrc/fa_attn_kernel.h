@@ -740,6 +740,30 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
     if constexpr (KX) score_extra(bk, s[0]);
   };
 
+  // S^T as scores, with the first NPRE operand fragments already in kpre
+  // (read before the softmax bookkeeping that precedes the MFMA block, so
+  // their LDS latency is hidden behind it)
+  constexpr int NPRE = (D == 256 ? 6 : 4) < NQC * NKB ? (D == 256 ? 6 : 4) : NQC * NKB;
+  auto k_frag = [&](const uint16_t* bk, int idx) -> u32x4 {
+    const int c = idx / NKB, kb = idx % NKB;
+    const int row = 32 * kb + j;
+    const int ch = 2 * (c + dh * NQC) + hl;
+    return *reinterpret_cast<const u32x4*>(&bk[row * D + 8 * (ch ^ swz_k<D>(row))]);
+  };
+  auto scores_pre = [&](const uint16_t* bk, f32x16 (&s)[NKB], const u32x4 (&kpre)[NPRE]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int idx = c * NKB + kb;
+        const u32x4 kw = idx < NPRE ? kpre[idx < NPRE ? idx : 0] : k_frag(bk, idx);
+        s[kb] = mfma32(as_bf16x8(kw), qf[c], s[kb]);
+      }
+    }
+  };
+
   // Mask values of the tile starting at key tb (MODS with a mask): for each
   // 8-key group r of block kb, the 4 bf16 at keys tb + 32 kb + 8 r + 4 hl ..
   // + 3 of this lane's row (the keys its score registers hold). Issued at the
@@ -1697,7 +1721,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           if (it + NBUF - 1 < n_tiles) issue_v(tb + (NBUF - 1) * BN, vbuf((u + NBUF - 1) % NBUF));
         }
         float nb = 0.f;
+        u32x4 kpre[kBig ? 1 : NPRE];
         if constexpr (!kBig) {
+#pragma unroll
+          for (int x = 0; x < NPRE; ++x) kpre[x] = k_frag(kbuf((u + 1) % NBUF), x);
           combine_partner(sc, it & 1);
           nb = prepare(sc, tb);
         }
@@ -1823,7 +1850,7 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           }
           __builtin_amdgcn_sched_barrier(0);
         } else {
-          scores(kbuf((u + 1) % NBUF), sn);    // tile t+1 (unused after the last tile)
+          scores_pre(kbuf((u + 1) % NBUF), sn, kpre);    // tile t+1 (unused after the last tile)
           if constexpr (kCopyInBlock) {
             static_assert(NBUF == 2, "copies into the buffers the step frees");
 #pragma unroll
@@ -1844,9 +1871,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           {
             // the operand reads as one stream over both phases (the PV
             // phase's first reads beside the last score MFMAs)
-            constexpr int kAh = D == 256 ? 6 : 4;
-            __builtin_amdgcn_sched_group_barrier(0x100, kAh, 0);
-            sched_cont<NKB * NQC, 1, NDB * NKS, 2, kAh, kExpValuPerTile / (NKB * NQC), -1, -1, 0>();
+            // (the first NPRE reads went out before the softmax bookkeeping)
+            sched_cont<NKB * NQC, 1, NDB * NKS, 2, NPRE, kExpValuPerTile / (NKB * NQC), -1, -1, 0>();
           }
         }
         if constexpr (kPrioMfma) __builtin_amdgcn_s_setprio(0);
