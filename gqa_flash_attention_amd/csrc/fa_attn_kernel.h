@@ -742,8 +742,10 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
 
   // S^T as scores, with the first NPRE operand fragments already in kpre
   // (read before the softmax bookkeeping that precedes the MFMA block, so
-  // their LDS latency is hidden behind it)
-  constexpr int NPRE = (D == 256 ? 6 : 4) < NQC * NKB ? (D == 256 ? 6 : 4) : NQC * NKB;
+  // their LDS latency is hidden behind it). Reads then run NPRE ahead of
+  // their MFMAs: at head dim 256 four measured 1-2 % faster than six and
+  // 3 % faster than eight (two and three: 8 % slower).
+  constexpr int NPRE = 4 < NQC * NKB ? 4 : NQC * NKB;
   auto k_frag = [&](const uint16_t* bk, int idx) -> u32x4 {
     const int c = idx / NKB, kb = idx % NKB;
     const int row = 32 * kb + j;
@@ -1867,9 +1869,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           accumulate(vbuf(u), pf);
           // one schedule for the whole step: S(t+1) MFMAs each followed by the
           // next K read and a share of tile t's exponentiation, then the PV
-          // MFMAs each followed by the next two V^T reads; reads run 4 ahead
-          // of their MFMAs, 6 at head dim 256 (one wave per SIMD, nothing
-          // else covers its LDS latency: measured 2 % faster; 8: no gain)
+          // MFMAs each followed by the next two V^T reads; reads run NPRE
+          // ahead of their MFMAs
           {
             // the operand reads as one stream over both phases (the PV
             // phase's first reads beside the last score MFMAs)
