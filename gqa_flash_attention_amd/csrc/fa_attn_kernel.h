@@ -1670,7 +1670,8 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
       //   spread to the end of the step made the next step wait for them
       //   (measured, C4B: top of the step 1.61 ms, two after every batch
       //   1.58, four after each score batch 1.55, eight after each of the
-      //   first two 1.47-1.52);
+      //   first two 1.47-1.52; the batches are now two MFMAs each, and the
+      //   copies go out after the first two of them);
       // * head dim 256: inside the MFMA block, after the scores' MFMAs are
       //   issued (C4A 0.215 -> 0.205 ms; after the softmax bookkeeping
       //   instead: no change);
@@ -1751,7 +1752,9 @@ __global__ void __launch_bounds__(NW * 64, WPE) attn_kernel(const AttnArgs a) {
           // S(t+1) batches.
           const uint16_t* bk = kbuf((u + 1) % NBUF);
           const uint16_t* bv = vbuf(u);
-          constexpr int KB = 4;                    // MFMAs per batch
+          // MFMAs per batch: two (measured against one, four and eight:
+          // C4B 1.461 -> 1.429 ms against four; one and eight 12-14 % slower)
+          constexpr int KB = 2;
           constexpr int NSB = NQC / KB;            // S batches
           constexpr int NPAIR = NKS * 4;           // exponentiated pairs per lane
           static_assert(NKB == 1 && NQC % KB == 0 && (NKS * NDB) % KB == 0, "head dim 512 tile shape");
